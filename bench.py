@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the MX hot path on one MI355X.
+
+One step = the whole path on one batch of synthetic input, for the MOSS
+two-level workload (M = N = K = 4096, A bf16 Student-t(3) activations with
+4 outlier K-channels x100, B bf16 N(0, 0.02) weights):
+  1. mx_quantize(A, row copy, E4M3, two-level: FP32 tensor scale + E8M0)
+  2. mx_quantize(B [K][N], column copy -> [N][K], same format)
+  3. mx_gemm(A, B) with the tensor scales applied once in the epilogue,
+     bf16 output.
+Inputs are resident in HBM before timing starts; a 512 MiB write evicts
+L2/MALL before every step (outside the timed kernels) so no step reads its
+inputs from cache.  Kernel times come from HIP events recorded on the stream
+the kernels run on.
+
+Prints one JSON line (rank 0).  `--workload` selects another workload for
+profiling runs; the default is the one above.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from fp4_quantization_block_amd import inputs as I  # noqa: E402
+from fp4_quantization_block_amd import mx  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0}   # dense scaled MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(x):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+class Timer:
+    """HIP events around launches on the current stream."""
+
+    def __init__(self):
+        self.samples = {}
+
+    def run(self, name, fn):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.samples.setdefault(name, []).append((s, e))
+        return out
+
+    def mean_ms(self, name):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.samples[name]]))
+
+
+# ------------------------------------------------------------------ workloads
+def setup_moss(args):
+    w = I.make("moss_two_level_4096")
+    A = to_dev(w.tensors["A"])            # [M][K]
+    B = to_dev(w.tensors["B"])            # [K][N]
+    M, K = A.shape
+    N = B.shape[1]
+    cfg = mx.qconfig("e4m3", two_level=True)
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N, K // 32), dtype=torch.uint8, device="cuda")
+    ta = torch.empty(1, dtype=torch.float32, device="cuda")
+    tb = torch.empty(1, dtype=torch.float32, device="cuda")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(t):
+        t.run("quant_A", lambda: mx.mx_quantize(A, mx.MX_AXIS_ROW, cfg, qa, sa, ta))
+        t.run("quant_B", lambda: mx.mx_quantize(B, mx.MX_AXIS_COL, cfg, qb, sb, tb))
+        t.run("gemm", lambda: mx.mx_gemm(qa, sa, ta, "e4m3", qb, sb, tb, "e4m3", M, N, K,
+                                         out_dtype=mx.MX_OUT_BF16, c=C))
+
+    flops = 2.0 * M * N * K
+    # algorithmic bytes of one two-level quantize of an R x C bf16 tensor:
+    # amax pass (2 B/elem) + quantize pass (2 B read + 1 B code + 1/32 B scale)
+    qbytes = lambda R, Cc: 2 * R * Cc + 2 * R * Cc + R * Cc + R * Cc // 32
+    info = dict(flops=flops, qbytes={"quant_A": qbytes(M, K), "quant_B": qbytes(K, N)},
+                gemm_kernel="gemm", mfma="fp8",
+                config={"workload": "moss_two_level_e4m3_gemm_4096", "M": M, "N": N, "K": K,
+                        "a": "bf16 student-t(3), 4 K-channels x100", "b": "bf16 N(0,0.02)",
+                        "elem": "e4m3", "scales": "fp32 tensor + e8m0 1x32", "out": "bf16"},
+                host=w.tensors)
+    return step, info
+
+
+def setup_dual(args):
+    w = I.make("dual_layout_16384x14336")
+    X = to_dev(w.tensors["X"])
+    R, Cc = X.shape
+    cfg = mx.qconfig("e4m3")
+    outs = [torch.empty((R, Cc), dtype=torch.uint8, device="cuda"),
+            torch.empty((R, Cc // 32), dtype=torch.uint8, device="cuda"),
+            torch.empty((Cc, R), dtype=torch.uint8, device="cuda"),
+            torch.empty((Cc, R // 32), dtype=torch.uint8, device="cuda")]
+
+    def step(t):
+        t.run("dual", lambda: mx.mx_quantize_dual_layout(X, cfg, *outs))
+
+    info = dict(flops=0.0, qbytes={"dual": 2 * R * Cc + 2 * R * Cc + 2 * R * Cc // 32},
+                gemm_kernel=None, mfma=None,
+                config={"workload": "dual_layout_e4m3_16384x14336", "R": R, "C": Cc},
+                host=w.tensors)
+    return step, info
+
+
+def setup_fp4(args):
+    w = I.make("mxfp4_wgrad_qkv")
+    dY = to_dev(w.tensors["dY"])          # [T][Q]
+    X = to_dev(w.tensors["X"])            # [T][H]
+    T, Q = dY.shape
+    H = X.shape[1]
+    cfg = mx.qconfig("e2m1", sr=True, hadamard=True, seed=I.SR_SEED)
+    qa = torch.empty((Q, T // 2), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((Q, T // 32), dtype=torch.uint8, device="cuda")
+    qb = torch.empty((H, T // 2), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((H, T // 32), dtype=torch.uint8, device="cuda")
+    C = torch.empty((Q, H), dtype=torch.bfloat16, device="cuda")
+
+    def step(t):
+        t.run("quant_dY", lambda: mx.mx_quantize(dY, mx.MX_AXIS_COL, cfg, qa, sa))
+        t.run("quant_X", lambda: mx.mx_quantize(X, mx.MX_AXIS_COL, cfg, qb, sb))
+        t.run("gemm", lambda: mx.mx_gemm(qa, sa, None, "e2m1", qb, sb, None, "e2m1", Q, H, T,
+                                         hadamard_k=True, out_dtype=mx.MX_OUT_BF16, c=C))
+
+    qb_ = lambda R, Cc: 2 * R * Cc + R * Cc // 2 + R * Cc // 32
+    info = dict(flops=2.0 * Q * H * T, qbytes={"quant_dY": qb_(T, Q), "quant_X": qb_(T, H)},
+                gemm_kernel="gemm", mfma="fp4",
+                config={"workload": "mxfp4_wgrad_qkv", "M": Q, "N": H, "K": T}, host=w.tensors)
+    return step, info
+
+
+WORKLOADS = {"moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4}
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline_moss(host, rows_sample=256):
+    """The oracle (plain C, all host cores) on a bounded sample of the step:
+    two-level quantization of the full A and B, and the GEMM for the first
+    `rows_sample` rows of C; the GEMM time is scaled to all M rows."""
+    import oracle as O
+    n = os.cpu_count() or 1
+    A, B = host["A"], host["B"]
+    M, K = A.shape
+    N = B.shape[1]
+    t0 = time.perf_counter()
+    qa, sa, ta = O.quantize(A, O.AXIS_ROW, "e4m3", two_level=1, nthreads=n)
+    qb, sb, tb = O.quantize(B, O.AXIS_COL, "e4m3", two_level=1, nthreads=n)
+    t1 = time.perf_counter()
+    O.gemm(qa[:rows_sample], sa[:rows_sample], ta, "e4m3", qb, sb, tb, "e4m3", rows_sample, N, K,
+           nthreads=n)
+    t2 = time.perf_counter()
+    step_s = (t1 - t0) + (t2 - t1) * (M / rows_sample)
+    return {"value": round(2.0 * M * N * K / step_s / 1e12, 6), "unit": "TFLOP/s", "cores": n,
+            "kind": "oracle",
+            "sample": f"two-level quantize of full A and B ({t1 - t0:.2f} s) + GEMM rows "
+                      f"0..{rows_sample - 1} of {M} ({t2 - t1:.2f} s, scaled x{M // rows_sample})"}
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="moss", choices=sorted(WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-flush", action="store_true")
+    args = p.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+    assert torch.cuda.is_available(), "needs a GPU"
+    mx.load()
+    log(f"workload {args.workload}: generating inputs")
+    step, info = WORKLOADS[args.workload](args)
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def one(t):
+        if flush is not None:
+            flush.zero_()
+        step(t)
+
+    warm = Timer()
+    for _ in range(args.warmup):
+        one(warm)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    t = Timer()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        one(t)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    names = list(t.samples)
+    kernel_ms = {n: t.mean_ms(n) for n in names}
+    step_ms = sum(kernel_ms.values())
+    log("per-call ms:", {k: round(v, 4) for k, v in kernel_ms.items()})
+
+    quant = {}
+    for n, b in info["qbytes"].items():
+        gbs = b / (kernel_ms[n] * 1e-3) / 1e9
+        quant[n] = {"ms": round(kernel_ms[n], 4), "GB/s": round(gbs, 1),
+                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(b)}
+    if info["gemm_kernel"]:
+        g_ms = kernel_ms[info["gemm_kernel"]]
+        g_tf = info["flops"] / (g_ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[info["mfma"]]
+        roofline = {"bound": "mfma", "achieved": round(g_tf, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(g_tf / peak, 4), "traffic": None,
+                    "kernel": f"k_gemm ({info['mfma']} scaled MFMA)",
+                    "algorithmic": f"{info['flops']:.4g} FLOP per launch"}
+        value = info["flops"] / (step_ms * 1e-3) / 1e12
+        metric = "MX GEMM TFLOP/s (% scaled-MFMA peak); mx_quantize GB/s (% HBM peak)"
+        unit = "TFLOP/s"
+    else:
+        n = names[0]
+        gbs = info["qbytes"][n] / (kernel_ms[n] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "k_quant dual layout"}
+        value = gbs
+        metric = "mx_quantize GB/s (% HBM peak)"
+        unit = "GB/s"
+    out = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "e4m3" if args.workload != "fp4" else "e2m1",
+           "data": "synthetic (seeded; no weights or datasets)",
+           "config": info["config"], "roofline": roofline,
+           "kernels": quant, "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+           "timing": "HIP events on the launch stream; L2/MALL flushed before each step (not timed)"}
+    if info["gemm_kernel"]:
+        out["kernels"]["gemm"] = {"ms": round(kernel_ms[info["gemm_kernel"]], 4),
+                                  "TFLOP/s": roofline["achieved"], "frac_mfma": roofline["frac"]}
+    if args.workload == "moss" and not args.no_cpu_baseline:
+        log("timing the oracle on the host (bounded sample)")
+        out["cpu_baseline"] = cpu_baseline_moss(info["host"])
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,186 @@
+// abi.cpp -- the C ABI of libmx.so (declared in include/mx.h).  Every entry
+// point validates its arguments on the host before touching HIP; on an
+// error it enqueues nothing and returns a status.  Nothing is allocated and
+// no state is kept between calls (apart from a thread-local error text).
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mx.h"
+#include "mx_internal.h"
+
+namespace {
+
+thread_local char g_msg[256] = "";
+
+mx_status fail(mx_status s, const char* what)
+{
+    std::snprintf(g_msg, sizeof g_msg, "%s", what);
+    return s;
+}
+
+mx_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return MX_OK;
+    std::snprintf(g_msg, sizeof g_msg, "HIP: %s", hipGetErrorString(e));
+    return MX_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_fmt(int32_t f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1; }
+int elem_bits(int32_t f) { return f == MX_E2M1 ? 4 : 8; }
+
+mx_status check_cfg(const mx_qconfig* cfg, const float* tensor_scale)
+{
+    if (!cfg) return fail(MX_ERR_INVALID_ARG, "cfg is NULL");
+    if (!valid_fmt(cfg->fmt)) return fail(MX_ERR_INVALID_ARG, "unknown element format");
+    if (cfg->block != 32) return fail(MX_ERR_INVALID_ARG, "block size must be 32");
+    if (cfg->scale_fmt != MX_SCALE_E8M0 && cfg->scale_fmt != MX_SCALE_E8M0_TENSOR_F32)
+        return fail(MX_ERR_INVALID_ARG, "unknown scale format");
+    if (cfg->tscale != MX_TSCALE_COMPUTE && cfg->tscale != MX_TSCALE_PROVIDED)
+        return fail(MX_ERR_INVALID_ARG, "unknown tensor-scale mode");
+    if (cfg->rounding != MX_RNE && cfg->rounding != MX_SR)
+        return fail(MX_ERR_INVALID_ARG, "unknown rounding mode");
+    if (cfg->hadamard != 0 && cfg->hadamard != 1) return fail(MX_ERR_INVALID_ARG, "hadamard must be 0 or 1");
+    if (cfg->reserved != 0) return fail(MX_ERR_INVALID_ARG, "reserved field must be 0");
+    if (cfg->scale_fmt == MX_SCALE_E8M0_TENSOR_F32 && !tensor_scale)
+        return fail(MX_ERR_INVALID_ARG, "two-level scaling needs tensor_scale");
+    if (cfg->scale_fmt == MX_SCALE_E8M0_TENSOR_F32 && (reinterpret_cast<uintptr_t>(tensor_scale) & 3u))
+        return fail(MX_ERR_ALIGNMENT, "tensor_scale must be 4-byte aligned");
+    return MX_OK;
+}
+
+mx_status check_source(const void* x, int32_t src, int64_t rows, int64_t cols, int64_t ld)
+{
+    if (!x) return fail(MX_ERR_INVALID_ARG, "x is NULL");
+    if (src != MX_SRC_F32 && src != MX_SRC_BF16) return fail(MX_ERR_INVALID_ARG, "unknown source dtype");
+    if (rows <= 0 || cols <= 0) return fail(MX_ERR_INVALID_ARG, "rows and cols must be > 0");
+    if (ld < cols) return fail(MX_ERR_INVALID_ARG, "ld must be >= cols");
+    const int64_t es = src == MX_SRC_F32 ? 4 : 2;
+    if (!aligned16(x) || (ld * es) % 16 != 0) return fail(MX_ERR_ALIGNMENT, "x and ld*elem_size must be 16-byte aligned");
+    return MX_OK;
+}
+
+mx::QuantJob make_job(const void* x, int32_t src, int64_t rows, int64_t cols, int64_t ld,
+                      const mx_qconfig* cfg, float* tensor_scale)
+{
+    mx::QuantJob j{};
+    j.x = x; j.src = src; j.rows = rows; j.cols = cols; j.ld = ld;
+    j.fmt = cfg->fmt;
+    j.sr = cfg->rounding == MX_SR;
+    j.hadamard = cfg->hadamard != 0;
+    j.two_level = cfg->scale_fmt == MX_SCALE_E8M0_TENSOR_F32 ? (cfg->tscale == MX_TSCALE_COMPUTE ? 1 : 2) : 0;
+    j.seed = cfg->seed;
+    j.offset = cfg->offset;
+    j.tensor_scale = tensor_scale;
+    return j;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_status_string(mx_status s)
+{
+    switch (s) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_INVALID_ARG: return "MX_ERR_INVALID_ARG";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
+    case MX_ERR_ALIGNMENT: return "MX_ERR_ALIGNMENT";
+    case MX_ERR_HIP: return "MX_ERR_HIP";
+    }
+    return "unknown mx_status";
+}
+
+const char* mx_last_error_message(void) { return g_msg; }
+
+mx_status mx_quantize(const void* x, int32_t src_dtype, int64_t rows, int64_t cols, int64_t ld,
+                      int32_t axis, const mx_qconfig* cfg, void* q, uint8_t* scales,
+                      float* tensor_scale, void* stream)
+{
+    g_msg[0] = '\0';
+    mx_status s = check_source(x, src_dtype, rows, cols, ld);
+    if (s != MX_OK) return s;
+    if ((s = check_cfg(cfg, tensor_scale)) != MX_OK) return s;
+    if (!q || !scales) return fail(MX_ERR_INVALID_ARG, "q or scales is NULL");
+    if (axis != MX_AXIS_ROW && axis != MX_AXIS_COL) return fail(MX_ERR_INVALID_ARG, "unknown axis");
+    if (axis == MX_AXIS_ROW && cols % 32 != 0) return fail(MX_ERR_INVALID_ARG, "row blocks need cols % 32 == 0");
+    if (axis == MX_AXIS_COL && rows % 32 != 0) return fail(MX_ERR_INVALID_ARG, "column blocks need rows % 32 == 0");
+    if (!aligned16(q)) return fail(MX_ERR_ALIGNMENT, "q must be 16-byte aligned");
+    mx::QuantJob j = make_job(x, src_dtype, rows, cols, ld, cfg, tensor_scale);
+    if (axis == MX_AXIS_ROW) { j.q_row = (uint8_t*)q; j.s_row = scales; }
+    else { j.q_col = (uint8_t*)q; j.s_col = scales; }
+    return hip_status(mx::launch_quantize(j, (hipStream_t)stream));
+}
+
+mx_status mx_quantize_dual_layout(const void* x, int32_t src_dtype, int64_t rows, int64_t cols,
+                                  int64_t ld, const mx_qconfig* cfg, void* q_row,
+                                  uint8_t* s_row, void* q_col, uint8_t* s_col,
+                                  float* tensor_scale, void* stream)
+{
+    g_msg[0] = '\0';
+    mx_status s = check_source(x, src_dtype, rows, cols, ld);
+    if (s != MX_OK) return s;
+    if ((s = check_cfg(cfg, tensor_scale)) != MX_OK) return s;
+    if (!q_row || !s_row || !q_col || !s_col) return fail(MX_ERR_INVALID_ARG, "an output pointer is NULL");
+    if (rows % 32 != 0 || cols % 32 != 0) return fail(MX_ERR_INVALID_ARG, "dual layout needs rows % 32 == 0 and cols % 32 == 0");
+    if (!aligned16(q_row) || !aligned16(q_col)) return fail(MX_ERR_ALIGNMENT, "q_row and q_col must be 16-byte aligned");
+    mx::QuantJob j = make_job(x, src_dtype, rows, cols, ld, cfg, tensor_scale);
+    j.q_row = (uint8_t*)q_row; j.s_row = s_row;
+    j.q_col = (uint8_t*)q_col; j.s_col = s_col;
+    return hip_status(mx::launch_quantize(j, (hipStream_t)stream));
+}
+
+mx_status mx_gemm(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,
+                  const void* qb, const uint8_t* sb, const float* tb, int32_t fb,
+                  int64_t M, int64_t N, int64_t K, float alpha, int32_t hadamard_k,
+                  void* c, int32_t out_dtype, int64_t ldc, void* stream)
+{
+    g_msg[0] = '\0';
+    if (!qa || !sa || !qb || !sb || !c) return fail(MX_ERR_INVALID_ARG, "an operand pointer is NULL");
+    if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(MX_ERR_INVALID_ARG, "unknown element format");
+    if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return fail(MX_ERR_INVALID_ARG, "unknown output dtype");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(MX_ERR_INVALID_ARG, "M, N, K must be > 0");
+    if (K % 32 != 0) return fail(MX_ERR_INVALID_ARG, "K must be a multiple of 32");
+    if (ldc < N) return fail(MX_ERR_INVALID_ARG, "ldc must be >= N");
+    if (hadamard_k != 0 && hadamard_k != 1) return fail(MX_ERR_INVALID_ARG, "hadamard_k must be 0 or 1");
+    if (elem_bits(fa) != elem_bits(fb)) return fail(MX_ERR_UNSUPPORTED, "mixed FP8 x FP4 operands are not built");
+    if (!aligned16(qa) || !aligned16(qb)) return fail(MX_ERR_ALIGNMENT, "qa and qb must be 16-byte aligned");
+    const uintptr_t es = out_dtype == MX_OUT_F32 ? 4 : 2;
+    if ((reinterpret_cast<uintptr_t>(c) % es) != 0) return fail(MX_ERR_ALIGNMENT, "c must be aligned to its element size");
+    if (((reinterpret_cast<uintptr_t>(ta) | reinterpret_cast<uintptr_t>(tb)) & 3u) != 0)
+        return fail(MX_ERR_ALIGNMENT, "ta and tb must be 4-byte aligned");
+    mx::GemmJob j{};
+    j.qa = (const uint8_t*)qa; j.sa = sa; j.ta = ta; j.fa = fa;
+    j.qb = (const uint8_t*)qb; j.sb = sb; j.tb = tb; j.fb = fb;
+    j.M = M; j.N = N; j.K = K;
+    j.alpha = alpha; j.hadamard_k = hadamard_k != 0;
+    j.c = c; j.out_dtype = out_dtype; j.ldc = ldc;
+    return hip_status(mx::launch_gemm(j, (hipStream_t)stream));
+}
+
+mx_status mx_dequantize(const void* q, const uint8_t* scales, const float* tensor_scale,
+                        int32_t fmt, int64_t rows, int64_t cols, int32_t axis, int32_t hadamard,
+                        void* out, int32_t out_dtype, void* stream)
+{
+    g_msg[0] = '\0';
+    if (!q || !scales || !out) return fail(MX_ERR_INVALID_ARG, "q, scales or out is NULL");
+    if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "unknown element format");
+    if (axis != MX_AXIS_ROW && axis != MX_AXIS_COL) return fail(MX_ERR_INVALID_ARG, "unknown axis");
+    if (hadamard != 0 && hadamard != 1) return fail(MX_ERR_INVALID_ARG, "hadamard must be 0 or 1");
+    if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return fail(MX_ERR_INVALID_ARG, "unknown output dtype");
+    if (rows <= 0 || cols <= 0) return fail(MX_ERR_INVALID_ARG, "rows and cols must be > 0");
+    if (axis == MX_AXIS_ROW && cols % 32 != 0) return fail(MX_ERR_INVALID_ARG, "row blocks need cols % 32 == 0");
+    if (axis == MX_AXIS_COL && rows % 32 != 0) return fail(MX_ERR_INVALID_ARG, "column blocks need rows % 32 == 0");
+    if (!aligned16(q) || !aligned16(out)) return fail(MX_ERR_ALIGNMENT, "q and out must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(tensor_scale) & 3u) return fail(MX_ERR_ALIGNMENT, "tensor_scale must be 4-byte aligned");
+    mx::DequantJob j{};
+    j.q = (const uint8_t*)q; j.scales = scales; j.tensor_scale = tensor_scale;
+    j.fmt = fmt; j.rows = rows; j.cols = cols; j.axis = axis; j.hadamard = hadamard != 0;
+    j.out = out; j.out_dtype = out_dtype;
+    return hip_status(mx::launch_dequantize(j, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// mx_device.h -- device helpers for the gfx950 MX kernels: element-format
+// traits, exact scaling, saturating round-to-nearest-even through the
+// hardware FP8/FP4 converters, software stochastic rounding, Philox4x32-10,
+// and the fixed-sign 32-point Hadamard butterfly.
+//
+// Sources (web pages; cited as [tag, section]):
+//   [MOSS] "MOSS: 用微缩放和自动缩放实现无损 FP8 训练，OLMo-7B 加速 34%"
+//   [FAF]  "格式感知融合:让FP4预训练提速两倍的工程实践"
+//   Element encodings and the shared-exponent rule: OCP Microscaling (MX)
+//   Formats specification v1.0.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+typedef short short2v __attribute__((ext_vector_type(2)));
+
+enum : int { E4M3 = 0, E5M2 = 1, E2M1 = 2 };
+enum : int { SRC_F32 = 0, SRC_BF16 = 1 };
+
+// Element-format traits.  emax: exponent of the largest finite value; emin:
+// exponent of the smallest normal; mbits: stored mantissa bits; fmax: the
+// largest finite value (E4M3 448, E5M2 57344, E2M1 6).
+template <int FMT> struct Fmt;
+template <> struct Fmt<E4M3> {
+    static constexpr int bits = 8, emax = 8, emin = -6, mbits = 3;
+    static constexpr float fmax = 448.0f;
+};
+template <> struct Fmt<E5M2> {
+    static constexpr int bits = 8, emax = 15, emin = -14, mbits = 2;
+    static constexpr float fmax = 57344.0f;
+};
+template <> struct Fmt<E2M1> {
+    static constexpr int bits = 4, emax = 2, emin = 0, mbits = 1;
+    static constexpr float fmax = 6.0f;
+};
+
+// 2^k as an fp32 for k in [-126, 127] (exact; built from the exponent field)
+__device__ __forceinline__ float exp2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
+// bf16 pair in one dword -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// |x| bits as an unsigned key: ordered like |x| for finite values, Inf above
+// every finite value and NaN above Inf.
+__device__ __forceinline__ uint32_t abs_key(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// OCP shared exponent from the block's |max| key: floor(log2(amax)) - emax,
+// clamped to [-127, 127]; -127 for an all-zero block.  Works on the fp32
+// exponent field, so fp32 subnormal maxima get their true exponent.
+template <int FMT>
+__device__ __forceinline__ int block_exponent(uint32_t amax_key)
+{
+    // a zero or fp32-subnormal maximum (exponent <= -127) always clamps to -127
+    const int ef = (int)(amax_key >> 23);
+    if (ef == 0) return -127;
+    int e = ef - 127 - Fmt<FMT>::emax;
+    e = e < -127 ? -127 : e;
+    return e;                      // <= 127 - emax for finite fp32 maxima
+}
+
+// v * 2^-e for a shared exponent of a finite block, e in [-127, 125]: one
+// multiply by a normal fp32 power of two.  Exact unless the result falls
+// below 2^-126, where every element format rounds it to a signed zero.
+__device__ __forceinline__ float scale_by(float v, int e) { return v * exp2i(-e); }
+
+// ---------------------------------------------------------------------
+// Encoding of already-scaled values.  The gfx950 converters round to
+// nearest-even exactly (including subnormal outputs and signed zero) but do
+// not saturate, so the value is clamped to +-fmax first, which gives the
+// saturating RNE of the OCP definition.
+// ---------------------------------------------------------------------
+template <int FMT>
+__device__ __forceinline__ float clamp_fmax(float y)
+{
+    return __builtin_amdgcn_fmed3f(y, -Fmt<FMT>::fmax, Fmt<FMT>::fmax);
+}
+
+// two FP8 codes (y0 -> low byte, y1 -> high byte) of a 16-bit lane
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt2_fp8(float y0, float y1)
+{
+    if constexpr (FMT == E4M3)
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false) & 0xFFFFu;
+    else
+        return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(y0, y1, 0, false) & 0xFFFFu;
+}
+
+// two FP4 codes (y0 -> low nibble, y1 -> high nibble) of a byte
+__device__ __forceinline__ uint32_t cvt2_fp4(float y0, float y1)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0) & 0xFFu;
+}
+
+// ---------------------------------------------------------------------
+// Stochastic rounding ([FAF, "两个关键的数值技巧"]): with lo <= |y| < hi the
+// neighbouring representable magnitudes and F = floor((|y|-lo)/(hi-lo) *
+// 2^32), round up iff u < F.  Returns the chosen value (exactly
+// representable, sign of y kept); |y| >= fmax saturates.
+// ---------------------------------------------------------------------
+template <int FMT>
+__device__ __forceinline__ float sr_value(float y, uint32_t u)
+{
+    const float a = fabsf(y);
+    float r;
+    if (a >= Fmt<FMT>::fmax) {
+        r = Fmt<FMT>::fmax;
+    } else {
+        const uint32_t ab = __float_as_uint(a);
+        const int ea = (int)(ab >> 23) - 127;                  // -127 for 0 / subnormal
+        const int eq = (ea > Fmt<FMT>::emin ? ea : Fmt<FMT>::emin) - Fmt<FMT>::mbits;  // quantum 2^eq
+        // lo: |y| truncated to a multiple of 2^eq
+        float lo;
+        const int drop = 23 - (ea - eq);                      // mantissa bits below the quantum
+        if (ea < eq || ab < 0x00800000u) lo = 0.0f;           // below one quantum (or fp32 subnormal)
+        else lo = __uint_as_float(ab & ~((1u << drop) - 1u));
+        const float d = (a - lo) * exp2i(32 - eq);            // exact, < 2^32
+        const uint32_t F = (uint32_t)d;                       // floor
+        r = (u < F) ? lo + exp2i(eq) : lo;
+    }
+    return __builtin_copysignf(r, y);
+}
+
+// ---------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11)
+// ---------------------------------------------------------------------
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; r++) {
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+        c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// Random word for the element with row-major source index idx: counter
+// (idx>>2 low, idx>>2 high, axis, offset), key (seed low, seed high), word idx&3.
+__device__ __forceinline__ u32x4 philox_block(uint64_t n, uint32_t axis, uint32_t offset,
+                                              uint32_t k0, uint32_t k1)
+{
+    return philox4x32_10(u32x4{(uint32_t)n, (uint32_t)(n >> 32), axis, offset}, k0, k1);
+}
+
+__device__ __forceinline__ uint32_t pick(const u32x4& w, uint32_t i)
+{
+    return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
+}
+
+// ---------------------------------------------------------------------
+// Fixed-sign 32-point Hadamard ([FAF, "两个关键的数值技巧"]): Sylvester
+// order, unnormalised, stages h = 1, 2, 4, 8, 16; at each stage the pair
+// (a, b) = (v[i], v[i+h]) becomes (a+b, a-b) in fp32.
+// ---------------------------------------------------------------------
+__device__ __forceinline__ void fwht32(float* v)
+{
+#pragma unroll
+    for (int st = 0; st < 5; st++) {
+        const int h = 1 << st;
+#pragma unroll
+        for (int i = 0; i < 32; i++)
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    }
+}
+
+}  // namespace mx

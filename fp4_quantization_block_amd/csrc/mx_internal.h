@@ -1,0 +1,44 @@
+// mx_internal.h -- host-side launchers shared by the ABI layer and the
+// kernel translation units.  Every launcher assumes its arguments were
+// validated by the ABI layer and returns the hipError_t of its launches.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+struct QuantJob {
+    const void* x;          // source tile, row stride ld elements
+    int src;                // SRC_F32 / SRC_BF16
+    int64_t rows, cols, ld;
+    int fmt;                // E4M3 / E5M2 / E2M1
+    bool sr, hadamard;
+    int two_level;          // 0 none, 1 s_t from the amax word, 2 s_t provided
+    uint64_t seed;
+    uint32_t offset;
+    uint8_t* q_row;  uint8_t* s_row;    // row copy (nullptr: not written)
+    uint8_t* q_col;  uint8_t* s_col;    // column copy (nullptr: not written)
+    float* tensor_scale;    // two-level: amax scratch / s_t
+};
+
+hipError_t launch_quantize(const QuantJob& j, hipStream_t stream);
+
+struct DequantJob {
+    const uint8_t* q; const uint8_t* scales; const float* tensor_scale;
+    int fmt; int64_t rows, cols; int axis; bool hadamard;
+    void* out; int out_dtype;
+};
+
+hipError_t launch_dequantize(const DequantJob& j, hipStream_t stream);
+
+struct GemmJob {
+    const uint8_t* qa; const uint8_t* sa; const float* ta; int fa;
+    const uint8_t* qb; const uint8_t* sb; const float* tb; int fb;
+    int64_t M, N, K;
+    float alpha; bool hadamard_k;
+    void* c; int out_dtype; int64_t ldc;
+};
+
+hipError_t launch_gemm(const GemmJob& j, hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,190 @@
+/*
+ * mx.h -- C ABI of libmx.so: MX (microscaling) quantization and the
+ * block-scaled low-precision GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited as [tag, section]):
+ *   [MOSS] "MOSS: 用微缩放和自动缩放实现无损 FP8 训练，OLMo-7B 加速 34%"
+ *          (blog.zhiliyouxian.com)
+ *   [FAF]  "格式感知融合:让FP4预训练提速两倍的工程实践" (kongchang.com)
+ *   [COAT] write-up of "COAT: Compressing Optimizer States and Activation
+ *          for memory efficient FP8 Training" (dignews.cc)
+ *   Element encodings and the shared-exponent rule: OCP Microscaling (MX)
+ *   Formats specification v1.0.
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library allocates no memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *     only enqueues work on it and returns without synchronizing; outputs
+ *     are valid once the stream reaches that point.
+ *   - Arguments are validated on the host before any HIP call; on any
+ *     error nothing is enqueued and the status says why.  No exceptions
+ *     cross the ABI.  MX_ERR_HIP reports a failed launch (text via
+ *     mx_last_error_message()).
+ *   - Calls on different streams that write the same buffers race; calls
+ *     on one stream are ordered.
+ */
+#ifndef MX_H
+#define MX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MX_OK = 0,
+    MX_ERR_INVALID_ARG = 1,   /* null pointer, bad enum, bad shape */
+    MX_ERR_UNSUPPORTED = 2,   /* a valid option this library does not build */
+    MX_ERR_ALIGNMENT = 3,     /* pointer / leading dimension not 16-byte aligned */
+    MX_ERR_HIP = 4            /* kernel launch failed */
+} mx_status;
+
+/* source dtype of the tensor being quantized */
+enum { MX_SRC_F32 = 0, MX_SRC_BF16 = 1 };
+
+/* element formats: FP8 E4M3 (max 448), FP8 E5M2 (max 57344), FP4 E2M1
+ * (max 6; 1 sign, 2 exponent, 1 mantissa bit [FAF, "FP4加速为何常常纸上富贵"]) */
+enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2 };
+
+/* scale formats: E8M0 power-of-two per 32-block only, or MOSS two-level:
+ * an FP32 per-tensor scale amax/Fmax on top of the E8M0 block scales
+ * ([MOSS, "创新 1：两级微缩放策略", "两级缩放实现"]) */
+enum { MX_SCALE_E8M0 = 0, MX_SCALE_E8M0_TENSOR_F32 = 1 };
+
+/* for the two-level format: compute the per-tensor scale from the tensor,
+ * or read a caller-provided one (e.g. a predicted weight scale,
+ * [MOSS, "创新 2：权重自动缩放"]) */
+enum { MX_TSCALE_COMPUTE = 0, MX_TSCALE_PROVIDED = 1 };
+
+/* rounding: round-to-nearest-even, or stochastic rounding driven by
+ * Philox4x32-10 ([FAF, "两个关键的数值技巧"]) */
+enum { MX_RNE = 0, MX_SR = 1 };
+
+/* block axis / stored layout of a quantized copy:
+ *   MX_AXIS_ROW: 1x32 blocks along each row; codes stored [rows][cols],
+ *                scales [rows][cols/32]
+ *   MX_AXIS_COL: 32x1 blocks down each column; the copy is stored
+ *                TRANSPOSED: codes [cols][rows], scales [cols][rows/32]
+ * FP4 codes are packed two per byte along the stored row, element 2j in
+ * the low nibble of byte j.  Stored rows are dense (no padding). */
+enum { MX_AXIS_ROW = 0, MX_AXIS_COL = 1 };
+
+/* output dtype of mx_gemm / mx_dequantize */
+enum { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 };
+
+typedef struct {
+    int32_t fmt;        /* MX_E4M3 / MX_E5M2 / MX_E2M1 */
+    int32_t block;      /* must be 32 */
+    int32_t scale_fmt;  /* MX_SCALE_E8M0 / MX_SCALE_E8M0_TENSOR_F32 */
+    int32_t tscale;     /* MX_TSCALE_COMPUTE / MX_TSCALE_PROVIDED (two-level only) */
+    int32_t rounding;   /* MX_RNE / MX_SR */
+    int32_t hadamard;   /* 1: fixed-sign 32-point Hadamard along the block axis first */
+    uint64_t seed;      /* SR: Philox key = (seed low 32, seed high 32) */
+    uint32_t offset;    /* SR: fourth Philox counter word */
+    uint32_t reserved;  /* must be 0 */
+} mx_qconfig;
+
+/*
+ * mx_quantize -- one quantized copy of a 2-D tensor.
+ *
+ * Per block of 32 elements along `axis` ([MOSS, "两级缩放实现"] for the
+ * steps, [FAF, "两个关键的数值技巧"] for SR and the Hadamard):
+ *   1. two-level only: s_t = amax(|x|)/Fmax (IEEE fp32 division; 1 if the
+ *      tensor is all zero) and x <- x / s_t (IEEE fp32 division);
+ *   2. if cfg->hadamard: v = H32 * block (unnormalised Sylvester FWHT in
+ *      fp32, stages 1,2,4,8,16);
+ *   3. e = floor(log2(max|v|)) - emax(fmt), clamped to [-127,127] (-127
+ *      for an all-zero block); scale byte = e + 127; a block holding a
+ *      NaN or Inf gets byte 0xFF and NaN codes (E2M1: 0);
+ *   4. y = v * 2^-e (exact); RNE, or SR: with lo <= |y| < hi the
+ *      neighbouring codes and F = floor((|y|-lo)/(hi-lo) * 2^32), round up
+ *      iff u < F, where u is word (idx & 3) of Philox4x32-10 with counter
+ *      (idx>>2 low, idx>>2 high, axis, offset), key (seed low, seed high)
+ *      and idx = r*cols + c the element's row-major index in the source;
+ *      |y| >= Fmax saturates to +-Fmax; the sign is kept (also for zero).
+ *
+ * x:     source, `src_dtype`, rows x cols with row stride `ld` elements;
+ *        16-byte aligned, ld*elem_size a multiple of 16, ld >= cols.
+ * rows, cols: > 0.  MX_AXIS_ROW needs cols % 32 == 0; MX_AXIS_COL needs
+ *        rows % 32 == 0.
+ * q, scales: the stored copy (layouts above); q 16-byte aligned.
+ * tensor_scale: one fp32 in device memory.  Two-level + COMPUTE: written
+ *        with s_t (used as scratch while the amax is reduced, so it must
+ *        not be read before the stream reaches the end of this call).
+ *        Two-level + PROVIDED: read.  MX_SCALE_E8M0: ignored (may be NULL).
+ * Errors: MX_ERR_INVALID_ARG (null pointers, block != 32, bad enum,
+ *        reserved != 0, shapes above), MX_ERR_ALIGNMENT, MX_ERR_HIP.
+ */
+mx_status mx_quantize(const void* x, int32_t src_dtype, int64_t rows, int64_t cols, int64_t ld,
+                      int32_t axis, const mx_qconfig* cfg, void* q, uint8_t* scales,
+                      float* tensor_scale, void* stream);
+
+/*
+ * mx_quantize_dual_layout -- both copies from one read of the source
+ * ([FAF, "格式感知融合的设计思路"]: the producer writes the layouts its
+ * consumers take, with no separate re-layout pass).  Same arithmetic as
+ * two mx_quantize calls (MX_AXIS_ROW into q_row/s_row, MX_AXIS_COL into
+ * q_col/s_col) with the same cfg; SR draws the two copies from
+ * independent streams (axis word 0 and 1).  Needs rows % 32 == 0 and
+ * cols % 32 == 0.  Errors as mx_quantize.
+ */
+mx_status mx_quantize_dual_layout(const void* x, int32_t src_dtype, int64_t rows, int64_t cols,
+                                  int64_t ld, const mx_qconfig* cfg, void* q_row,
+                                  uint8_t* s_row, void* q_col, uint8_t* s_col,
+                                  float* tensor_scale, void* stream);
+
+/*
+ * mx_gemm -- C = alpha' * A . B^T on scaled codes ([MOSS, "GEMM Kernel
+ * 优化"]: the main loop multiplies codes with their block scales applied by
+ * the matrix instruction; the per-tensor scales are applied once, in the
+ * epilogue).
+ *
+ * qa, sa: A as written by the quantizer, [M][K] codes (K contiguous) and
+ *         [M][K/32] E8M0 scales, element format fa.
+ * qb, sb: B as [N][K] codes and [N][K/32] scales, element format fb.
+ *         (A weight W[K][N] quantized with MX_AXIS_COL is exactly this.)
+ * ta, tb: device fp32 per-tensor scales or NULL (= 1).
+ * alpha' = alpha * ta * tb * (hadamard_k ? 1/32 : 1); set hadamard_k iff
+ *         both operands were quantized with the Hadamard along K (H.H^T =
+ *         32 I).  Accumulation is fp32.
+ * c:      [M][N] with row stride ldc >= N elements, MX_OUT_F32 or
+ *         MX_OUT_BF16 (round to nearest even).
+ * Supported pairs: fa, fb both FP8 (E4M3/E5M2 in any combination) or
+ *         both E2M1.  M, N > 0; K > 0 and K % 32 == 0.
+ * Errors: MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED (mixed FP8/FP4),
+ *         MX_ERR_ALIGNMENT (qa, qb not 16-byte aligned), MX_ERR_HIP.
+ */
+mx_status mx_gemm(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,
+                  const void* qb, const uint8_t* sb, const float* tb, int32_t fb,
+                  int64_t M, int64_t N, int64_t K, float alpha, int32_t hadamard_k,
+                  void* c, int32_t out_dtype, int64_t ldc, void* stream);
+
+/*
+ * mx_dequantize -- inverse of mx_quantize ([MOSS, "两级缩放实现"]:
+ * micro-scale first, then the tensor scale): per element
+ * decode(code) * 2^(byte-127) (exact in fp32), then, if `hadamard`, the
+ * inverse transform FWHT32(.) * 1/32 along the block, then, if
+ * tensor_scale != NULL, one fp32 multiply by *tensor_scale.
+ * q, scales: a copy in the stored layout of `axis` for a rows x cols source.
+ * out: rows x cols in the SOURCE layout (row-major, dense), MX_OUT_F32 or
+ *      MX_OUT_BF16.
+ * Shapes as mx_quantize.  Errors: MX_ERR_INVALID_ARG, MX_ERR_ALIGNMENT
+ * (q not 16-byte aligned), MX_ERR_HIP.
+ */
+mx_status mx_dequantize(const void* q, const uint8_t* scales, const float* tensor_scale,
+                        int32_t fmt, int64_t rows, int64_t cols, int32_t axis, int32_t hadamard,
+                        void* out, int32_t out_dtype, void* stream);
+
+/* Static text for a status code. */
+const char* mx_status_string(mx_status status);
+
+/* Text of the last MX_ERR_HIP / validation failure on the calling thread
+ * (empty string if none).  Valid until the next call on this thread. */
+const char* mx_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MX_H */

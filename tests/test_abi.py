@@ -1,0 +1,126 @@
+"""The C ABI on the CPU: libmx.so loads, exports every function declared in
+include/mx.h, and rejects bad arguments before any HIP call (so these calls
+are safe without a GPU: nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_quantization_block_amd import mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mx.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:mx_status|const char\*)\s+(mx_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mx.LIB_PATH):
+        pytest.skip("libmx.so not built")
+    return mx.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(mx.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s, name in enumerate(["MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_UNSUPPORTED",
+                              "MX_ERR_ALIGNMENT", "MX_ERR_HIP"]):
+        assert lib.mx_status_string(s).decode() == name
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails first
+FAKE_ODD = 0x10008
+
+
+def _q(lib, x=FAKE, src=1, rows=64, cols=64, ld=64, axis=0, cfg=None, q=FAKE, s=FAKE, ts=None):
+    cfg = cfg if cfg is not None else mx.qconfig("e4m3")
+    return lib.mx_quantize(x, src, rows, cols, ld, axis, ctypes.byref(cfg), q, s, ts, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), mx.MX_ERR_INVALID_ARG),
+    (dict(q=None), mx.MX_ERR_INVALID_ARG),
+    (dict(s=None), mx.MX_ERR_INVALID_ARG),
+    (dict(src=7), mx.MX_ERR_INVALID_ARG),
+    (dict(rows=0), mx.MX_ERR_INVALID_ARG),
+    (dict(cols=-3), mx.MX_ERR_INVALID_ARG),
+    (dict(ld=32), mx.MX_ERR_INVALID_ARG),
+    (dict(axis=2), mx.MX_ERR_INVALID_ARG),
+    (dict(cols=48, ld=48), mx.MX_ERR_INVALID_ARG),              # row blocks need cols % 32
+    (dict(axis=1, rows=40), mx.MX_ERR_INVALID_ARG),             # col blocks need rows % 32
+    (dict(x=FAKE_ODD), mx.MX_ERR_ALIGNMENT),
+    (dict(ld=68), mx.MX_ERR_ALIGNMENT),                         # 68 * 2 bytes not 16-aligned
+    (dict(q=FAKE_ODD), mx.MX_ERR_ALIGNMENT),
+])
+def test_quantize_validation(lib, kw, status):
+    assert _q(lib, **kw) == status
+    assert lib.mx_last_error_message().decode() != ""
+
+
+@pytest.mark.parametrize("field,value", [("fmt", 9), ("block", 16), ("scale_fmt", 5),
+                                         ("tscale", 3), ("rounding", 4), ("hadamard", 2),
+                                         ("reserved", 1)])
+def test_quantize_bad_config(lib, field, value):
+    cfg = mx.qconfig("e2m1")
+    setattr(cfg, field, value)
+    assert _q(lib, cfg=cfg) == mx.MX_ERR_INVALID_ARG
+
+
+def test_two_level_needs_tensor_scale(lib):
+    cfg = mx.qconfig("e4m3", two_level=True)
+    assert _q(lib, cfg=cfg, ts=None) == mx.MX_ERR_INVALID_ARG
+    assert _q(lib, cfg=cfg, ts=FAKE + 2) == mx.MX_ERR_ALIGNMENT
+    assert lib.mx_quantize(FAKE, 1, 64, 64, 64, 0, None, FAKE, FAKE, None, None) == mx.MX_ERR_INVALID_ARG
+
+
+def test_dual_layout_validation(lib):
+    cfg = mx.qconfig("e4m3")
+    f = lib.mx_quantize_dual_layout
+    assert f(FAKE, 1, 40, 64, 64, ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, None, None) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 1, 64, 40, 40, ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, None, None) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 1, 64, 64, 64, ctypes.byref(cfg), FAKE, FAKE, None, FAKE, None, None) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 1, 64, 64, 64, ctypes.byref(cfg), FAKE, FAKE, FAKE_ODD, FAKE, None, None) == mx.MX_ERR_ALIGNMENT
+
+
+def _g(lib, qa=FAKE, sa=FAKE, ta=None, fa=0, qb=FAKE, sb=FAKE, tb=None, fb=0, M=64, N=64, K=64,
+       alpha=1.0, hk=0, c=FAKE, out=1, ldc=64):
+    return lib.mx_gemm(qa, sa, ta, fa, qb, sb, tb, fb, M, N, K, alpha, hk, c, out, ldc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qa=None), mx.MX_ERR_INVALID_ARG),
+    (dict(sb=None), mx.MX_ERR_INVALID_ARG),
+    (dict(c=None), mx.MX_ERR_INVALID_ARG),
+    (dict(fa=5), mx.MX_ERR_INVALID_ARG),
+    (dict(out=3), mx.MX_ERR_INVALID_ARG),
+    (dict(M=0), mx.MX_ERR_INVALID_ARG),
+    (dict(K=48), mx.MX_ERR_INVALID_ARG),
+    (dict(ldc=32), mx.MX_ERR_INVALID_ARG),
+    (dict(hk=2), mx.MX_ERR_INVALID_ARG),
+    (dict(fa=0, fb=2), mx.MX_ERR_UNSUPPORTED),
+    (dict(qa=FAKE_ODD), mx.MX_ERR_ALIGNMENT),
+    (dict(c=FAKE + 1), mx.MX_ERR_ALIGNMENT),
+    (dict(ta=FAKE + 2), mx.MX_ERR_ALIGNMENT),
+])
+def test_gemm_validation(lib, kw, status):
+    assert _g(lib, **kw) == status
+
+
+def test_dequantize_validation(lib):
+    f = lib.mx_dequantize
+    assert f(None, FAKE, None, 0, 64, 64, 0, 0, FAKE, 0, None) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, 7, 64, 64, 0, 0, FAKE, 0, None) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, 0, 64, 48, 0, 0, FAKE, 0, None) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, 0, 40, 64, 1, 0, FAKE, 0, None) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, 0, 64, 64, 0, 0, FAKE_ODD, 0, None) == mx.MX_ERR_ALIGNMENT
+    assert f(FAKE, FAKE, None, 0, 64, 64, 0, 3, FAKE, 0, None) == mx.MX_ERR_INVALID_ARG

@@ -1,0 +1,252 @@
+"""GPU parity of the quantizers (mx_quantize, mx_quantize_dual_layout)
+against the CPU oracle: bit-exact codes, scale bytes, stochastic-rounding
+outputs and per-tensor scales.
+
+Small cases cover every element format x source dtype x layout x option
+(RNE / SR / Hadamard / two-level) on ragged shapes that do not fill the
+kernels' tiles, with wide-dynamic-range data holding zeros, signed zeros,
+subnormals and representable midpoints.  The five workloads run at full size
+in the launch configuration the benchmark uses and are compared in full
+where the oracle is fast enough, otherwise on sampled blocks (corners
+included).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_quantization_block_amd import inputs as I
+from fp4_quantization_block_amd import mx
+from gpu_util import (DEV, assert_codes_equal, assert_same_f32, log, require_gpu, sampled_codes,
+                      to_device, u8)
+
+pytestmark = pytest.mark.gpu
+
+SEED = I.SR_SEED
+FMTS = ["e4m3", "e5m2", "e2m1"]
+OPTIONS = {
+    "rne": dict(),
+    "sr": dict(sr=True),
+    "had": dict(hadamard=True),
+    "two": dict(two_level=True),
+    "sr_had_two": dict(sr=True, hadamard=True, two_level=True),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def edge_rich(rng, rows, cols, src):
+    """Normal values with row- and column-wise magnitudes over ~2^+-60, plus
+    zeros, negative zeros, fp32/bf16 subnormals and code midpoints."""
+    x = rng.standard_normal((rows, cols))
+    x *= np.exp2(rng.integers(-60, 60, size=(rows, 1)))
+    x *= np.exp2(rng.integers(-4, 5, size=(1, cols)))
+    m = rng.random((rows, cols))
+    x[m < 0.04] = 0.0
+    x[(m >= 0.04) & (m < 0.06)] = -0.0
+    sub = (m >= 0.06) & (m < 0.08)
+    x[sub] = rng.standard_normal(sub.sum()) * 2.0 ** -140
+    mid = (m >= 0.08) & (m < 0.10)
+    x[mid] = np.sign(rng.standard_normal(mid.sum())) * (1.0 + 1.0 / 16) * 2.0 ** rng.integers(-8, 8, mid.sum())
+    x = x.astype(np.float32)
+    return I.to_bf16_bits(x) if src == "bf16" else x
+
+
+def run_gpu(xd, mode, fmt, opts):
+    cfg = mx.qconfig(fmt, two_level=opts.get("two_level", False), sr=opts.get("sr", False),
+                     hadamard=opts.get("hadamard", False), seed=SEED, offset=7)
+    if mode == "dual":
+        qr, sr_, qc, sc, ts = mx.mx_quantize_dual_layout(xd, cfg)
+        torch.cuda.synchronize()
+        return (u8(qr), u8(sr_)), (u8(qc), u8(sc)), ts
+    axis = mx.MX_AXIS_ROW if mode == "row" else mx.MX_AXIS_COL
+    q, s, ts = mx.mx_quantize(xd, axis, cfg)
+    torch.cuda.synchronize()
+    out = (u8(q), u8(s))
+    return (out, None, ts) if mode == "row" else (None, out, ts)
+
+
+def run_oracle(x, axis, fmt, opts):
+    q, s, st = O.quantize(x, axis, fmt, two_level=1 if opts.get("two_level") else 0,
+                          sr=opts.get("sr", False), hadamard=opts.get("hadamard", False),
+                          seed=SEED, offset=7)
+    return q, s, st
+
+
+SHAPES = {"row": (45, 160), "col": (96, 37), "dual": (160, 288)}
+
+
+@pytest.mark.parametrize("opt", list(OPTIONS))
+@pytest.mark.parametrize("mode", ["row", "col", "dual"])
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_small_all_options(fmt, src, mode, opt):
+    opts = OPTIONS[opt]
+    rows, cols = SHAPES[mode]
+    rng = np.random.default_rng(zlib.crc32(f"{fmt}{src}{mode}{opt}".encode()))
+    x = edge_rich(rng, rows, cols, src)
+    row, col, ts = run_gpu(to_device(x), mode, fmt, opts)
+    if row is not None:
+        q, s, st = run_oracle(x, O.AXIS_ROW, fmt, opts)
+        assert_codes_equal(row[0], q, "row codes")
+        assert_codes_equal(row[1], s, "row scales")
+    if col is not None:
+        q, s, st = run_oracle(x, O.AXIS_COL, fmt, opts)
+        assert_codes_equal(col[0], q, "col codes")
+        assert_codes_equal(col[1], s, "col scales")
+    if opts.get("two_level"):
+        assert_same_f32(ts.cpu().numpy(), [st])
+
+
+def test_nonfinite_and_degenerate_blocks():
+    x = np.ones((64, 64), np.float32)
+    x[0, 3] = np.nan                      # NaN block (row 0, cols 0-31; col 3, rows 0-31)
+    x[33, 40] = -np.inf
+    x[40:, :] = 0.0                       # all-zero blocks
+    x[34, :] = -0.0
+    x[35, :32] = 2.0 ** -149              # smallest fp32 subnormal
+    x[36, :32] = 3.4e38                   # near fp32 max
+    x[37, :32] = 240.0                    # 1.875 * 2^7: saturates in E4M3
+    for fmt in FMTS:
+        for opts in (dict(), dict(sr=True), dict(hadamard=True)):
+            row, col, _ = run_gpu(to_device(x), "dual", fmt, opts)
+            q, s, _ = run_oracle(x, O.AXIS_ROW, fmt, opts)
+            assert_codes_equal(row[0], q, f"{fmt} {opts} row codes")
+            assert_codes_equal(row[1], s, f"{fmt} {opts} row scales")
+            q, s, _ = run_oracle(x, O.AXIS_COL, fmt, opts)
+            assert_codes_equal(col[0], q, f"{fmt} {opts} col codes")
+            assert_codes_equal(col[1], s, f"{fmt} {opts} col scales")
+
+
+def test_two_level_special_tensors():
+    for fill in (0.0, np.nan, np.inf):
+        x = np.full((32, 64), 1.5, np.float32)
+        x[5, 7] = fill
+        if fill == 0.0:
+            x[:] = 0.0
+        for mode in ("row", "col"):
+            row, col, ts = run_gpu(to_device(x), mode, "e4m3", dict(two_level=True))
+            got = row if mode == "row" else col
+            q, s, st = run_oracle(x, O.AXIS_ROW if mode == "row" else O.AXIS_COL, "e4m3",
+                                  dict(two_level=True))
+            assert_codes_equal(got[0], q, f"fill {fill} codes")
+            assert_codes_equal(got[1], s, f"fill {fill} scales")
+            assert_same_f32(ts.cpu().numpy(), [st])
+
+
+def test_provided_tensor_scale():
+    rng = np.random.default_rng(3)
+    x = I.to_bf16_bits(rng.standard_normal((64, 96)).astype(np.float32) * 30)
+    st = np.float32(0.0371)
+    ts = torch.tensor([st], dtype=torch.float32, device=DEV)
+    cfg = mx.qconfig("e4m3", two_level=True, tscale_provided=True)
+    q, s, _ = mx.mx_quantize(to_device(x), mx.MX_AXIS_ROW, cfg, tensor_scale=ts)
+    qo, so, _ = O.quantize(x, O.AXIS_ROW, "e4m3", two_level=2, tensor_scale=float(st))
+    assert_codes_equal(u8(q), qo, "codes")
+    assert_codes_equal(u8(s), so, "scales")
+    assert ts.item() == st                # provided scale is read, not written
+
+
+def test_strided_source():
+    """ld > cols: only the first cols of each row are quantized."""
+    rng = np.random.default_rng(4)
+    full = rng.standard_normal((64, 160)).astype(np.float32)
+    xd = to_device(full)[:, :96]
+    q, s, _ = mx.mx_quantize(xd, mx.MX_AXIS_ROW, mx.qconfig("e2m1", sr=True, seed=SEED))
+    qo, so, _ = O.quantize(np.ascontiguousarray(full[:, :96]), O.AXIS_ROW, "e2m1", sr=True, seed=SEED)
+    assert_codes_equal(u8(q), qo, "codes")
+    assert_codes_equal(u8(s), so, "scales")
+
+
+def test_deterministic_repeat():
+    rng = np.random.default_rng(5)
+    x = to_device(edge_rich(rng, 256, 512, "bf16"))
+    cfg = mx.qconfig("e2m1", sr=True, hadamard=True, seed=SEED)
+    a = mx.mx_quantize_dual_layout(x, cfg)
+    b = mx.mx_quantize_dual_layout(x, cfg)
+    for u, v in zip(a[:4], b[:4]):
+        assert torch.equal(u, v)
+
+
+# ------------------------------------------------------------------ full-size workloads
+def _sampled_compare(x, xd_out, axis, fmt, n, rng, **kw):
+    """Compare n random blocks (plus corners) of a stored GPU copy with the oracle."""
+    q_gpu, s_gpu = xd_out
+    rows, cols = x.shape
+    r0, c0 = I.sample_blocks(rng, rows, cols, 0 if axis == O.AXIS_ROW else 1, n)
+    codes, scales = O.quantize_blocks(x, axis, fmt, r0, c0, seed=SEED, **kw)
+    if axis == O.AXIS_ROW:
+        orow, oblk = r0, c0 // 32
+    else:
+        orow, oblk = c0, r0 // 32
+    got = sampled_codes(q_gpu, fmt, orow, oblk)
+    assert_codes_equal(got, codes, f"sampled {fmt} axis {axis} codes")
+    got_s = s_gpu[torch.from_numpy(orow).to(DEV), torch.from_numpy(oblk).to(DEV)].cpu().numpy().view(np.uint8)
+    assert np.array_equal(got_s, scales), "sampled scales differ"
+
+
+def test_full_mxfp8_gemm_256_operands():
+    w = I.make("mxfp8_gemm_256")
+    A, B = w.tensors["A"], w.tensors["B"]
+    qa, sa, _ = mx.mx_quantize(to_device(A), mx.MX_AXIS_ROW, mx.qconfig("e4m3"))
+    qb, sb, _ = mx.mx_quantize(to_device(B), mx.MX_AXIS_COL, mx.qconfig("e4m3"))
+    q, s, _ = O.quantize(A, O.AXIS_ROW, "e4m3")
+    assert_codes_equal(u8(qa), q, "A codes"); assert_codes_equal(u8(sa), s, "A scales")
+    q, s, _ = O.quantize(B, O.AXIS_COL, "e4m3")
+    assert_codes_equal(u8(qb), q, "B codes"); assert_codes_equal(u8(sb), s, "B scales")
+
+
+def test_full_moss_two_level_4096_operands():
+    w = I.make("moss_two_level_4096")
+    A, B = w.tensors["A"], w.tensors["B"]
+    cfg = mx.qconfig("e4m3", two_level=True)
+    qa, sa, ta = mx.mx_quantize(to_device(A), mx.MX_AXIS_ROW, cfg)
+    qb, sb, tb = mx.mx_quantize(to_device(B), mx.MX_AXIS_COL, cfg)
+    torch.cuda.synchronize()
+    q, s, st = O.quantize(A, O.AXIS_ROW, "e4m3", two_level=1)
+    assert_same_f32(ta.cpu().numpy(), [st])
+    assert_codes_equal(u8(qa), q, "A codes"); assert_codes_equal(u8(sa), s, "A scales")
+    q, s, st = O.quantize(B, O.AXIS_COL, "e4m3", two_level=1)
+    assert_same_f32(tb.cpu().numpy(), [st])
+    assert_codes_equal(u8(qb), q, "B codes"); assert_codes_equal(u8(sb), s, "B scales")
+
+
+def test_full_dual_layout_16384x14336_sampled():
+    w = I.make("dual_layout_16384x14336")
+    X = w.tensors["X"]
+    log("dual 16384x14336: generated")
+    qr, sr_, qc, sc, _ = mx.mx_quantize_dual_layout(to_device(X), mx.qconfig("e4m3"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(55)
+    _sampled_compare(X, (qr, sr_), O.AXIS_ROW, "e4m3", 3000, rng)
+    _sampled_compare(X, (qc, sc), O.AXIS_COL, "e4m3", 3000, rng)
+
+
+def test_full_mxfp4_wgrad_sampled():
+    w = I.make("mxfp4_wgrad_qkv")
+    cfg = mx.qconfig("e2m1", sr=True, hadamard=True, seed=SEED, offset=0)
+    rng = np.random.default_rng(44)
+    for name in ("dY", "X"):
+        x = w.tensors[name]
+        q, s, _ = mx.mx_quantize(to_device(x), mx.MX_AXIS_COL, cfg)
+        torch.cuda.synchronize()
+        _sampled_compare(x, (q, s), O.AXIS_COL, "e2m1", 3000, rng, sr=True, hadamard=True)
+        log("wgrad", name, "ok")
+
+
+def test_full_llama3_8b_mlp_dual_sampled():
+    w = I.make("llama3_8b_mlp")
+    rng = np.random.default_rng(33)
+    for name, fmt in (("X", "e4m3"), ("W_gu", "e4m3"), ("Xp", "e4m3"), ("W_d", "e4m3"),
+                      ("dY_gu", "e5m2"), ("dY_d", "e5m2")):
+        x = w.tensors[name]
+        qr, sr_, qc, sc, _ = mx.mx_quantize_dual_layout(to_device(x), mx.qconfig(fmt))
+        torch.cuda.synchronize()
+        _sampled_compare(x, (qr, sr_), O.AXIS_ROW, fmt, 1500, rng)
+        _sampled_compare(x, (qc, sc), O.AXIS_COL, fmt, 1500, rng)
+        log("mlp", name, "ok")
