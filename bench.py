@@ -145,7 +145,23 @@ def setup_fp4(args):
     return step, info
 
 
-WORKLOADS = {"moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4}
+def setup_copy(args):
+    """A plain 512 MiB device copy: the reference that scales the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) of a profiling run."""
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+
+    def step(t):
+        t.run("copy", lambda: dst.copy_(src))
+
+    info = dict(flops=0.0, qbytes={"copy": 2 * n}, gemm_kernel=None, mfma=None,
+                config={"workload": "device_copy_512MiB", "bytes_read": n, "bytes_written": n},
+                host={})
+    return step, info
+
+
+WORKLOADS = {"moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4, "copy": setup_copy}
 
 
 # ------------------------------------------------------------------ CPU baseline

@@ -4,6 +4,7 @@ Each source is compiled with hipcc in parallel, then linked into
 fp4_quantization_block_amd/libmx.so.  IEEE semantics are kept (no fast-math,
 fp32 denormals as the target default); packed-fp32 instructions are disabled.
 """
+import ctypes
 import os
 import shutil
 import subprocess
@@ -53,6 +54,8 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # resolve every symbol now: a missing kernel stub must fail the build
+    ctypes.CDLL(os.path.abspath(tmp), mode=os.RTLD_NOW)
     os.replace(tmp, LIB)
     return LIB
 

@@ -58,8 +58,8 @@ mx_status check_source(const void* x, int32_t src, int64_t rows, int64_t cols, i
     if (src != MX_SRC_F32 && src != MX_SRC_BF16) return fail(MX_ERR_INVALID_ARG, "unknown source dtype");
     if (rows <= 0 || cols <= 0) return fail(MX_ERR_INVALID_ARG, "rows and cols must be > 0");
     if (ld < cols) return fail(MX_ERR_INVALID_ARG, "ld must be >= cols");
-    const int64_t es = src == MX_SRC_F32 ? 4 : 2;
-    if (!aligned16(x) || (ld * es) % 16 != 0) return fail(MX_ERR_ALIGNMENT, "x and ld*elem_size must be 16-byte aligned");
+    const uintptr_t es = src == MX_SRC_F32 ? 4 : 2;
+    if (reinterpret_cast<uintptr_t>(x) % es != 0) return fail(MX_ERR_ALIGNMENT, "x must be aligned to its element size");
     return MX_OK;
 }
 

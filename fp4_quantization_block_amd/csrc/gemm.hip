@@ -13,20 +13,30 @@
 // (K contiguous codes, [rows][K/32] E8M0 scales).
 //
 // Tiling: 256x256 output tile per 256-thread workgroup (2x2 waves, 128x128
-// per wave = 4x4 MFMA 32x32 tiles with fp32 accumulators); K advances 128
-// bytes per row per stage (128 FP8 / 256 FP4 elements); A and B stages are
-// double-buffered in LDS (2 x 64 KiB + scales) with an XOR swizzle of the
-// 16-byte chunks to keep ds_read_b128 conflict-free.
+// per wave = 4x4 MFMA 32x32 tiles, fp32 accumulators in AGPRs).  K advances
+// 128 bytes per row per stage (128 FP8 / 256 FP4 elements).  Stages are
+// double-buffered in LDS and filled by direct global->LDS loads
+// (global_load_lds_dwordx4: lane i of a wave writes bytes [16i, 16i+16) of a
+// 1 KiB run), so operand tiles never pass through VGPRs.  The 16-byte chunks
+// of each 128-byte LDS row are XOR-swizzled by (row >> 1) & 7 -- applied on the
+// global side by choosing which chunk each lane fetches -- which keeps the
+// ds_read_b128 operand fetches free of bank conflicts.  A ragged last K
+// stage (K not a multiple of the stage) is loaded through registers with
+// zero fill.
 //
 // Operand lane layout of the 32x32x64 scaled MFMA (lane l, h = l / 32, row
-// or column l % 32):
+// or column l % 32), established with on-device probes:
 //   FP8: bytes 0-15 hold K [16h, 16h+16), bytes 16-31 hold K [32+16h, ...);
 //        the scale of K-block b (b = 0, 1) comes from lane (row + 32 b).
 //   FP4: 16 bytes hold K [32h, 32h+32), element 2j in the low nibble of
 //        byte j; the lane's own scale covers its block.
 // Either way lane l supplies the scale byte of block (2*kstep + h) of its
-// row, which is what the scale registers below carry.
-// Accumulator layout: register r of lane l is C[8(r/4) + 4h + r%4][l%32].
+// row.  Accumulator register r of lane l is C[8(r/4) + 4h + r%4][l%32].
+//
+// Workgroup order: workgroups are dealt round-robin to the 8 XCDs (each
+// with its own L2); the tile order below gives each XCD a compact block of
+// tiles (4 tile rows x 8 tile columns when the grid allows), so the A rows
+// and B columns one XCD streams are shared by its tiles through its L2.
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -36,11 +46,12 @@ namespace {
 
 typedef int int8v __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = 256, BN = 256;
 constexpr int BKB = 128;                  // bytes of K per row per stage
 constexpr int TILE_BYTES = BM * BKB;      // 32 KiB per operand per stage
-constexpr int SCALE_BYTES_MAX = 8;        // scale bytes per row per stage (FP4)
+constexpr int GROUP_M = 4;                // tile rows per ordering group
 
 struct GArgs {
     const uint8_t* qa; const uint8_t* sa; const float* ta;
@@ -49,15 +60,19 @@ struct GArgs {
     float alpha; int hadamard_k;
     void* c; int64_t ldc;
     int tiles_m, tiles_n;
+    int reg_path;             // 1: scale arrays not 4-byte aligned -> every stage via registers
 };
 
-// MFMA format codes: 0 = E4M3, 1 = E5M2, 4 = E2M1
 template <int FMT> struct MfmaFmt;
 template <> struct MfmaFmt<E4M3> { static constexpr int code = 0; };
 template <> struct MfmaFmt<E5M2> { static constexpr int code = 1; };
 template <> struct MfmaFmt<E2M1> { static constexpr int code = 4; };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ (row & 7)) << 4); }
+// LDS byte offset of 16-byte chunk `chunk` of tile row `row`.  The XOR key (row >> 1) & 7
+// together with the row parity spreads 16 consecutive rows over all 64 banks,
+// so the 16 lanes a ds_read_b128 serves per cycle never collide.
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ swz_key(row)) << 4); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
@@ -66,48 +81,169 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
     return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
+// tile index of this workgroup: XCD-aware, then grouped row-major order
+__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& tm, int& tn)
+{
+    const int total = tiles_m * tiles_n;
+    int t = wg;
+    if (total % 8 == 0) {                     // workgroup wg runs on XCD wg % 8
+        const int per = total / 8;
+        t = (wg % 8) * per + wg / 8;
+    }
+    const int group = GROUP_M * tiles_n;
+    const int g = t / group;
+    const int first = g * GROUP_M;
+    const int rows = min(GROUP_M, tiles_m - first);
+    const int in = t - g * group;
+    tm = first + in % rows;
+    tn = in / rows;
+}
+
+// Ties the accumulators to this point of the program: the MFMA builtins
+// have no side effects, so without it the compiler may sink a stage's MFMAs
+// past the end-of-stage wait and barrier, which serializes the loads.
+__device__ __forceinline__ void pin(f16v (&acc)[4][4])
+{
+#if defined(__HIP_DEVICE_COMPILE__)      // AGPR constraint: device pass only
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) asm volatile("" : "+a"(acc[i][j]));
+#endif
+}
+
+// One LDS stage of MFMAs for a wave's 128x128 sub-tile (4x4 tiles of 32x32).
+template <int FA, int FB>
+__device__ __forceinline__ void mma_stage(f16v (&acc)[4][4], const uint8_t* sA, const uint8_t* sB,
+                                          const uint32_t* sSA, const uint32_t* sSB, int wm, int wn,
+                                          int h, int l32)
+{
+    constexpr bool FP4 = (FA == E2M1);
+    constexpr int EPB = FP4 ? 2 : 1;
+    constexpr int SB = BKB * EPB / 32;               // scale bytes per row per stage (4 or 8)
+    constexpr int KSTEPS = BKB * EPB / 64;           // MFMA k-steps per stage (2 or 4)
+    // scale registers: the lane's row, shifted so block (2*ks + h) sits at
+    // byte 2*(ks%2) of dword ks/2
+    uint32_t sca[4][SB / 4], scb[4][SB / 4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int w = 0; w < SB / 4; w++) {
+            sca[i][w] = sSA[w * BM + wm * 128 + i * 32 + l32] >> (8 * h);
+            scb[i][w] = sSB[w * BM + wn * 128 + i * 32 + l32] >> (8 * h);
+        }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks++) {
+        int8v fa[4], fb[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int ra_row = wm * 128 + i * 32 + l32;
+            const int rb_row = wn * 128 + i * 32 + l32;
+            if constexpr (!FP4) {
+                const uint4 a0 = *(const uint4*)(sA + swz(ra_row, ks * 4 + h));
+                const uint4 a1 = *(const uint4*)(sA + swz(ra_row, ks * 4 + 2 + h));
+                const uint4 b0 = *(const uint4*)(sB + swz(rb_row, ks * 4 + h));
+                const uint4 b1 = *(const uint4*)(sB + swz(rb_row, ks * 4 + 2 + h));
+                fa[i] = int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                fb[i] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            } else {
+                const uint4 a0 = *(const uint4*)(sA + swz(ra_row, ks * 2 + h));
+                const uint4 b0 = *(const uint4*)(sB + swz(rb_row, ks * 2 + h));
+                fa[i] = int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+                fb[i] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int w = ks / 2;                     // scale dword
+                if ((ks & 1) == 0)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fa[i], fb[j], acc[i][j], MfmaFmt<FA>::code, MfmaFmt<FB>::code,
+                        0, (int)sca[i][w], 0, (int)scb[j][w]);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fa[i], fb[j], acc[i][j], MfmaFmt<FA>::code, MfmaFmt<FB>::code,
+                        2, (int)sca[i][w], 2, (int)scb[j][w]);
+            }
+    }
+}
+
 template <int FA, int FB, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm(GArgs g)
 {
+#if defined(__HIP_DEVICE_COMPILE__)      // the host pass only needs the launch stub
     constexpr bool FP4 = (FA == E2M1);
     constexpr int EPB = FP4 ? 2 : 1;                 // elements per byte
     constexpr int SB = BKB * EPB / 32;               // scale bytes per row per stage (4 or 8)
     constexpr int KSTEPS = BKB * EPB / 64;           // MFMA k-steps per stage (2 or 4)
 
-    extern __shared__ __align__(16) uint8_t smem[];
-    // stage buffers: [A0 B0 A1 B1] tiles, then [SA0 SB0 SA1 SB1] scales
-    auto sA = [&](int buf) { return smem + buf * 2 * TILE_BYTES; };
-    auto sB = [&](int buf) { return smem + buf * 2 * TILE_BYTES + TILE_BYTES; };
-    auto sSA = [&](int buf) { return smem + 4 * TILE_BYTES + buf * 2 * BM * SCALE_BYTES_MAX; };
-    auto sSB = [&](int buf) { return smem + 4 * TILE_BYTES + buf * 2 * BM * SCALE_BYTES_MAX + BM * SCALE_BYTES_MAX; };
+    // Two stage buffers as distinct LDS objects: the compiler can then see
+    // that fragment reads of one buffer do not depend on the direct loads
+    // still filling the other, and does not wait for them.
+    __shared__ __align__(16) uint8_t lA0[TILE_BYTES], lA1[TILE_BYTES];
+    __shared__ __align__(16) uint8_t lB0[TILE_BYTES], lB1[TILE_BYTES];
+    __shared__ __align__(16) uint32_t lSA0[2 * BM], lSA1[2 * BM], lSB0[2 * BM], lSB1[2 * BM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
 
-    // workgroup -> tile: consecutive ids run down a band of 8 tile rows so the
-    // A rows and B columns a wave of workgroups touches stay in L2
-    const int wg = blockIdx.x;
-    const int band = 8;
-    const int tiles_in_band = band * g.tiles_n;
-    const int b_idx = wg / tiles_in_band;
-    const int in_band = wg - b_idx * tiles_in_band;
-    const int band_rows = min(band, g.tiles_m - b_idx * band);
-    const int tm = b_idx * band + in_band % band_rows;
-    const int tn = in_band / band_rows;
+    int tm, tn;
+    tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
     const int64_t kbytes = g.K / EPB;                // bytes per operand row
     const int64_t kblocks = g.K / 32;
     const int nstages = (int)((kbytes + BKB - 1) / BKB);
+    const bool ragged = (kbytes % BKB) != 0;
 
-    // ---- global -> register staging (8 chunks of 16 B per operand per thread) ----
-    uint4 ra[8], rb[8];
-    uint32_t rsa[SB / 4], rsb[SB / 4];
-
-    auto load_stage = [&](int s) {
+    // ---- stage loads ----
+    // direct: bounds-checked buffer loads straight into LDS.  Wave w, load p
+    // covers tile rows 32p + 8w .. +8; lane -> row (lane / 8) of that run and
+    // LDS slot (lane % 8), which receives global chunk slot ^ (row & 7).  The
+    // buffer of load p starts at tile row 32p of the stage and ends at row M
+    // (N), so rows past the matrix read as zero.  Only the lane's 32-bit
+    // offset lives in a VGPR.
+    const int lrow = 8 * wave + (lane >> 3);                  // row within a 32-row run
+    const uint32_t voff = (uint32_t)(lrow * kbytes + (((lane & 7) ^ swz_key(lrow)) << 4));
+    const uint32_t soff_row = (uint32_t)((64 * wave + lane) * kblocks);
+    auto rsrc = [&](const uint8_t* base, int64_t first_row, int64_t rows, int64_t row_bytes,
+                    int64_t col0) {
+        int64_t n = (rows - first_row) * row_bytes - col0;
+        n = n < 0 ? 0 : (n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + first_row * row_bytes + col0),
+                                                 (short)0, (int)(uint32_t)n, 0x00020000);
+    };
+    auto load_direct = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) {
+        const int64_t kb0 = (int64_t)s * BKB;
+        const auto ra = rsrc(g.qa, m0, g.M, kbytes, kb0);
+        const auto rb = rsrc(g.qb, n0, g.N, kbytes, kb0);
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            const uint32_t off = voff + (uint32_t)(32 * p * kbytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + (32 * p + 8 * wave) * BKB), 16,
+                                                     off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sB + (32 * p + 8 * wave) * BKB), 16,
+                                                     off, 0, 0, 0);
+        }
+        // scales: plane w holds bytes [4w, 4w+4) of every row's stage scales
+#pragma unroll
+        for (int w = 0; w < SB / 4; w++) {
+            const int64_t blk = (int64_t)s * SB + 4 * w;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(g.sa, m0, g.M, kblocks, blk),
+                                                     (lds_void*)(sSA + w * BM + 64 * wave), 4,
+                                                     soff_row, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(g.sb, n0, g.N, kblocks, blk),
+                                                     (lds_void*)(sSB + w * BM + 64 * wave), 4,
+                                                     soff_row, 0, 0, 0);
+        }
+    };
+    // register path with zero fill for a ragged last stage
+    auto load_tail = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) {
         const int64_t kb0 = (int64_t)s * BKB;
 #pragma unroll
         for (int p = 0; p < 8; p++) {
@@ -115,45 +251,33 @@ void k_gemm(GArgs g)
             const int row = id >> 3, chunk = id & 7;
             const int64_t kb = kb0 + chunk * 16;
             const int64_t ar = min(m0 + row, g.M - 1), br = min(n0 + row, g.N - 1);
+            uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
             if (kb < kbytes) {
-                ra[p] = *(const uint4*)(g.qa + ar * kbytes + kb);
-                rb[p] = *(const uint4*)(g.qb + br * kbytes + kb);
-            } else {
-                ra[p] = make_uint4(0, 0, 0, 0);
-                rb[p] = make_uint4(0, 0, 0, 0);
+                va = *(const uint4*)(g.qa + ar * kbytes + kb);
+                vb = *(const uint4*)(g.qb + br * kbytes + kb);
             }
+            *(uint4*)(sA + swz(row, chunk)) = va;
+            *(uint4*)(sB + swz(row, chunk)) = vb;
         }
-        // scales: one row per thread
-        const int64_t blk0 = (int64_t)s * SB;
         const int64_t ar = min(m0 + tid, g.M - 1), br = min(n0 + tid, g.N - 1);
 #pragma unroll
         for (int w = 0; w < SB / 4; w++) {
             uint32_t va = 0, vb = 0;
 #pragma unroll
             for (int b = 0; b < 4; b++) {
-                const int64_t blk = blk0 + w * 4 + b;
+                const int64_t blk = (int64_t)s * SB + 4 * w + b;
                 const uint32_t xa = blk < kblocks ? g.sa[ar * kblocks + blk] : 127u;
                 const uint32_t xb = blk < kblocks ? g.sb[br * kblocks + blk] : 127u;
                 va |= xa << (8 * b);
                 vb |= xb << (8 * b);
             }
-            rsa[w] = va;
-            rsb[w] = vb;
+            sSA[w * BM + tid] = va;
+            sSB[w * BM + tid] = vb;
         }
     };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int p = 0; p < 8; p++) {
-            const int id = p * 256 + tid;
-            const int row = id >> 3, chunk = id & 7;
-            *(uint4*)(sA(buf) + swz(row, chunk)) = ra[p];
-            *(uint4*)(sB(buf) + swz(row, chunk)) = rb[p];
-        }
-#pragma unroll
-        for (int w = 0; w < SB / 4; w++) {
-            ((uint32_t*)(sSA(buf) + tid * SCALE_BYTES_MAX))[w] = rsa[w];
-            ((uint32_t*)(sSB(buf) + tid * SCALE_BYTES_MAX))[w] = rsb[w];
-        }
+    auto load_stage = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) {
+        if (g.reg_path || (ragged && s == nstages - 1)) load_tail(s, sA, sB, sSA, sSB);
+        else load_direct(s, sA, sB, sSA, sSB);
     };
 
     f16v acc[4][4];
@@ -164,102 +288,90 @@ void k_gemm(GArgs g)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-    load_stage(0);
-    store_stage(0);
+    load_stage(0, lA0, lB0, lSA0, lSB0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    for (int s = 0; s < nstages; s++) {
-        const int buf = s & 1;
-        if (s + 1 < nstages) load_stage(s + 1);
-
-        // scale registers: lane's row, shifted so block (2*ks + h) sits at byte 2*(ks%2)
-        uint32_t sca[4][SB / 4], scb[4][SB / 4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int ra_row = wm * 128 + i * 32 + l32;
-            const int rb_row = wn * 128 + i * 32 + l32;
-#pragma unroll
-            for (int w = 0; w < SB / 4; w++) {
-                sca[i][w] = ((const uint32_t*)(sSA(buf) + ra_row * SCALE_BYTES_MAX))[w] >> (8 * h);
-                scb[i][w] = ((const uint32_t*)(sSB(buf) + rb_row * SCALE_BYTES_MAX))[w] >> (8 * h);
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ks++) {
-            int8v fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int ra_row = wm * 128 + i * 32 + l32;
-                const int rb_row = wn * 128 + i * 32 + l32;
-                if constexpr (!FP4) {
-                    const uint4 a0 = *(const uint4*)(sA(buf) + swz(ra_row, ks * 4 + h));
-                    const uint4 a1 = *(const uint4*)(sA(buf) + swz(ra_row, ks * 4 + 2 + h));
-                    const uint4 b0 = *(const uint4*)(sB(buf) + swz(rb_row, ks * 4 + h));
-                    const uint4 b1 = *(const uint4*)(sB(buf) + swz(rb_row, ks * 4 + 2 + h));
-                    fa[i] = int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                    fb[i] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-                } else {
-                    const uint4 a0 = *(const uint4*)(sA(buf) + swz(ra_row, ks * 2 + h));
-                    const uint4 b0 = *(const uint4*)(sB(buf) + swz(rb_row, ks * 2 + h));
-                    fa[i] = int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
-                    fb[i] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int w = ks / 2;                 // scale dword
-                    if ((ks & 1) == 0)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fa[i], fb[j], acc[i][j], MfmaFmt<FA>::code, MfmaFmt<FB>::code,
-                            0, (int)sca[i][w], 0, (int)scb[j][w]);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fa[i], fb[j], acc[i][j], MfmaFmt<FA>::code, MfmaFmt<FB>::code,
-                            2, (int)sca[i][w], 2, (int)scb[j][w]);
-                }
-        }
-        if (s + 1 < nstages) store_stage(buf ^ 1);
+    int s = 0;
+    for (; s + 1 < nstages; s += 2) {
+        // even stage in buffer 0 while stage s+1 streams into buffer 1
+        load_stage(s + 1, lA1, lB1, lSA1, lSB1);
+        mma_stage<FA, FB>(acc, lA0, lB0, lSA0, lSB0, wm, wn, h, l32);
+        pin(acc);                                  // keep this stage's MFMAs before the wait
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // odd stage in buffer 1 while stage s+2 streams into buffer 0
+        if (s + 2 < nstages) load_stage(s + 2, lA0, lB0, lSA0, lSB0);
+        mma_stage<FA, FB>(acc, lA1, lB1, lSA1, lSB1, wm, wn, h, l32);
+        pin(acc);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
+    if (s < nstages) mma_stage<FA, FB>(acc, lA0, lB0, lSA0, lSB0, wm, wn, h, l32);   // odd count
 
     // ---- epilogue: per-tensor scales once ----
     float ap = g.alpha;
     if (g.ta) ap = ap * *g.ta;
     if (g.tb) ap = ap * *g.tb;
     if (g.hadamard_k) ap = ap * 0.03125f;
+
+    if constexpr (OUT == 1) {
+        // bf16: each wave stages its 128x128 sub-tile (256-byte rows) in its
+        // own 32 KiB of LDS, then writes 16-byte runs of 8 columns
+        uint8_t* region = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
+        uint16_t* ct = (uint16_t*)region;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int64_t col = n0 + wn * 128 + j * 32 + l32;
+            for (int j = 0; j < 4; j++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                if (row < g.M && col < g.N) {
-                    const float v = acc[i][j][r] * ap;
-                    if constexpr (OUT == 0) ((float*)g.c)[row * g.ldc + col] = v;
-                    else ((uint16_t*)g.c)[row * g.ldc + col] = f32_to_bf16_rne(v);
+                for (int r = 0; r < 16; r++) {
+                    const int row = i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                    const int col = j * 32 + l32;
+                    ct[row * 128 + col] = f32_to_bf16_rne(acc[i][j][r] * ap);
                 }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        const bool vec = (g.ldc % 8) == 0 && (((uintptr_t)g.c) & 15u) == 0;
+        const int64_t rbase = m0 + wm * 128, cbase = n0 + wn * 128;
+#pragma unroll 4
+        for (int p = 0; p < 32; p++) {
+            const int id = p * 64 + lane;
+            const int row = id >> 4, c8 = (id & 15) * 8;
+            const int64_t grow = rbase + row, gcol = cbase + c8;
+            if (grow >= g.M) continue;
+            const uint4 v = *(const uint4*)(ct + row * 128 + c8);
+            uint16_t* dst = (uint16_t*)g.c + grow * g.ldc + gcol;
+            if (vec && gcol + 8 <= g.N) {
+                *(uint4*)dst = v;
+            } else {
+                const uint16_t* e = (const uint16_t*)&v;
+                for (int k = 0; k < 8; k++)
+                    if (gcol + k < g.N) dst[k] = e[k];
             }
         }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int64_t col = n0 + wn * 128 + j * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                    if (row < g.M && col < g.N) ((float*)g.c)[row * g.ldc + col] = acc[i][j][r] * ap;
+                }
+            }
+    }
+#endif
 }
-
-constexpr size_t kSmemBytes = 4 * TILE_BYTES + 4 * BM * SCALE_BYTES_MAX;   // 136 KiB
 
 template <int FA, int FB, int OUT>
 hipError_t launch3(const GArgs& a, hipStream_t s)
 {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_gemm<FA, FB, OUT>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     const unsigned nwg = (unsigned)(a.tiles_m * a.tiles_n);
-    k_gemm<FA, FB, OUT><<<dim3(nwg), dim3(256), kSmemBytes, s>>>(a);
+    k_gemm<FA, FB, OUT><<<dim3(nwg), dim3(256), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -281,6 +393,7 @@ hipError_t launch_gemm(const GemmJob& j, hipStream_t stream)
     a.c = j.c; a.ldc = j.ldc;
     a.tiles_m = (int)((j.M + BM - 1) / BM);
     a.tiles_n = (int)((j.N + BN - 1) / BN);
+    a.reg_path = (((uintptr_t)j.sa | (uintptr_t)j.sb) & 3u) != 0;
     if (j.fa == E2M1) return launch2<E2M1, E2M1>(a, j.out_dtype, stream);
     if (j.fa == E4M3 && j.fb == E4M3) return launch2<E4M3, E4M3>(a, j.out_dtype, stream);
     if (j.fa == E5M2 && j.fb == E4M3) return launch2<E5M2, E4M3>(a, j.out_dtype, stream);

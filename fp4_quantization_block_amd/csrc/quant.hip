@@ -13,11 +13,23 @@
 //   [MOSS] "MOSS: 用微缩放和自动缩放实现无损 FP8 训练，OLMo-7B 加速 34%"
 //   [FAF]  "格式感知融合:让FP4预训练提速两倍的工程实践"
 //
-// Work decomposition of the general kernel: a 256-thread workgroup is four
-// waves stacked along the rows; each wave owns a 32-row strip and each lane a
-// 32-row x 4-column sub-tile held in registers.  Column blocks (32x1) are
-// then entirely inside one lane; row blocks (1x32) span 8 adjacent lanes and
-// are reduced with cross-lane shuffles.
+// Kernels
+//   k_quant_row   row copy only: one thread per 1x32 block, read straight
+//                 from global memory (64 contiguous bytes per lane for bf16),
+//                 no cross-lane traffic.
+//   k_quant_tile  column copy, or both copies from one read: a 256-thread
+//                 workgroup stages a 64-row x 128-column tile in LDS (rows
+//                 padded to keep the two access patterns bank-conflict free),
+//                 then each thread quantizes one 1x32 row block and/or one
+//                 32x1 column block.  Column copies are stored transposed.
+//                 For stochastic rounding of column blocks the workgroup
+//                 first generates the tile's Philox words cooperatively into
+//                 LDS, one 4-word block per call, so no word is wasted.
+//   k_amax_partial / k_amax_reduce   level-1 tensor amax for the two-level
+//                 scheme: per-workgroup partial maxima, then one workgroup
+//                 writes s_t = amax / Fmax.  The partials are parked in the
+//                 caller's scale array, which the quantize kernel overwrites
+//                 afterwards (no atomics, no extra memory).
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -25,17 +37,18 @@ namespace mx {
 
 namespace {
 
-constexpr int kSubW = 4;          // columns per lane
-constexpr int kWaves = 4;         // waves per workgroup (stacked along rows)
+constexpr int TR = 64, TC = 128;           // tile of k_quant_tile
+constexpr int LDSW = TC + 4;               // padded LDS row (floats)
 
 struct QArgs {
     const void* x;
     int64_t rows, cols, ld;
     uint8_t* q_row; uint8_t* s_row;
     uint8_t* q_col; uint8_t* s_col;
-    const float* tscale;
+    const float* tscale;          // s_t (two-level), read by the quantize kernels
     uint32_t k0, k1, offset;
     int sr, hadamard, two_level;
+    int vec;                      // 1: x and every row start are 16-byte aligned
 };
 
 // FP32 tensor scale s_t = amax / Fmax (IEEE division); 1 for an all-zero
@@ -48,284 +61,341 @@ __device__ __forceinline__ float tensor_scale_from_key(uint32_t key)
     return __uint_as_float(key) / Fmt<FMT>::fmax;
 }
 
-template <int FMT>
-__device__ __forceinline__ float load_tensor_scale(const QArgs& a)
+// x / s_t rounded to nearest even, with s_t fixed for the whole tensor.  The
+// reciprocal r = RN(1/s_t) is formed once; q = RN(x r) refined by one exact
+// residual step q' = RN(q + RN(x - q s_t) r) equals the IEEE quotient
+// whenever |x|, |q'| >= 2^-96 and |q'| <= 2^17 (the quantizer has |x| <= amax =
+// Fmax s_t, so |x / s_t| <= 57344); other operands, zeros included, take the
+// IEEE division.  (Checked exhaustively over every fp32 x for a set of
+// divisors with adversarial significands.)
+struct TensorDiv {
+    float s, r;
+    bool fast;      // s and 1/s are normal fp32 numbers
+};
+
+__device__ __forceinline__ TensorDiv make_div(float s)
 {
-    if (a.two_level == 1) return tensor_scale_from_key<FMT>(*(const uint32_t*)a.tscale);
-    return *a.tscale;
+    const float as = fabsf(s);
+    return TensorDiv{s, 1.0f / s, as > 0x1p-125f && as < 0x1p125f};
 }
 
-// code for an element of a NaN/Inf block: the format's NaN with the
-// element's sign (FP8), 0 (FP4, which has no NaN)
-template <int FMT>
-__device__ __forceinline__ uint32_t nan_code(float v)
+__device__ __forceinline__ float div_ts(float x, const TensorDiv& d)
 {
-    if constexpr (FMT == E2M1) return 0u;
-    return 0x7Fu | ((__float_as_uint(v) >> 24) & 0x80u);
+    if (!d.fast) return x / d.s;
+    float q = x * d.r;
+    const float rem = __builtin_fmaf(-q, d.s, x);
+    q = __builtin_fmaf(rem, d.r, q);
+    if (!(fabsf(q) >= 0x1p-96f && fabsf(q) <= 0x1p17f) || fabsf(x) < 0x1p-96f) q = x / d.s;
+    return q;
 }
 
-template <int SRC, int FMT, bool ROW, bool COL>
-__global__ __launch_bounds__(256) void k_quant(QArgs a)
+// Quantizes one 32-element block v (already divided by s_t, Hadamard not yet
+// applied).  u[i]: the element's random word (SR only).  Writes 8 (FP8) or 4
+// (FP4) packed dwords of codes; returns the scale byte.  A block holding a
+// NaN or Inf gets byte 0xFF and the format's canonical NaN code 0x7F for
+// every element (E2M1, which has no NaN: 0) -- the sign of a NaN produced by
+// arithmetic is not defined by IEEE 754, so no sign is carried.
+template <int FMT>
+__device__ __forceinline__ uint32_t quantize_block(float (&v)[32], bool had, bool sr,
+                                                   const uint32_t* u, uint32_t* out)
 {
-    constexpr int W = kSubW;
     constexpr int BITS = Fmt<FMT>::bits;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t r0 = ((int64_t)blockIdx.y * kWaves + wave) * 32;
-    if (r0 >= a.rows) return;                       // no LDS / barriers in this kernel
-    const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * W;
-    const int ncol = c0 < a.cols ? (int)(a.cols - c0 < W ? a.cols - c0 : W) : 0;
-    const int nrow = (int)(a.rows - r0 < 32 ? a.rows - r0 : 32);
-
-    // ---- load the 32 x W sub-tile (zero outside the tensor) ----
-    float v[32][W];
+    if (had) fwht32(v);
+    uint32_t key = 0;
+#pragma unroll
+    for (int i = 0; i < 32; i++) key = max(key, abs_key(v[i]));
+    if (key >= 0x7F800000u) {
+        constexpr uint32_t fill = BITS == 8 ? 0x7F7F7F7Fu : 0u;
+#pragma unroll
+        for (int k = 0; k < (BITS == 8 ? 8 : 4); k++) out[k] = fill;
+        return 0xFFu;
+    }
+    const int e = block_exponent<FMT>(key);
+    float y[32];
 #pragma unroll
     for (int i = 0; i < 32; i++) {
-        const int64_t base = (r0 + i) * a.ld + c0;
-        if (i < nrow && ncol == W) {
+        const float t = scale_by(v[i], e);
+        y[i] = sr ? sr_value<FMT>(t, u[i]) : clamp_fmax<FMT>(t);
+    }
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            out[k] = cvt2_fp8<FMT>(y[4 * k], y[4 * k + 1]) | (cvt2_fp8<FMT>(y[4 * k + 2], y[4 * k + 3]) << 16);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            out[k] = cvt2_fp4(y[8 * k], y[8 * k + 1]) | (cvt2_fp4(y[8 * k + 2], y[8 * k + 3]) << 8) |
+                     (cvt2_fp4(y[8 * k + 4], y[8 * k + 5]) << 16) | (cvt2_fp4(y[8 * k + 6], y[8 * k + 7]) << 24);
+    }
+    return (uint32_t)(e + 127);
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_codes(uint8_t* dst, const uint32_t* w)
+{
+    *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+    if constexpr (BITS == 8) *(uint4*)(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+template <int SRC>
+__device__ __forceinline__ float load1(const void* x, int64_t i)
+{
+    if constexpr (SRC == SRC_BF16) return __uint_as_float((uint32_t)((const uint16_t*)x)[i] << 16);
+    else return ((const float*)x)[i];
+}
+
+// ---------------------------------------------------------------------------
+// Row copy: one thread per 1x32 block.  Grid: x covers the blocks of a row
+// in runs of 64 (one per lane), y covers rows four at a time (one per wave).
+// ---------------------------------------------------------------------------
+template <int SRC, int FMT>
+__global__ __launch_bounds__(256) void k_quant_row(QArgs a)
+{
+    constexpr int BITS = Fmt<FMT>::bits;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t nblk = a.cols / 32;
+    const int64_t cb = (int64_t)blockIdx.x * 64 + lane;
+    if (cb >= nblk) return;
+    const TensorDiv d = make_div(a.two_level ? *a.tscale : 1.0f);
+    for (int64_t r = (int64_t)blockIdx.y * 4 + wave; r < a.rows; r += (int64_t)gridDim.y * 4) {
+        const int64_t base = r * a.ld + cb * 32;
+        float v[32];
+        if (a.vec) {
             if constexpr (SRC == SRC_BF16) {
-                const uint2 w = *(const uint2*)((const uint16_t*)a.x + base);
-                v[i][0] = bf16_lo(w.x); v[i][1] = bf16_hi(w.x);
-                v[i][2] = bf16_lo(w.y); v[i][3] = bf16_hi(w.y);
+                const uint4* p = (const uint4*)((const uint16_t*)a.x + base);
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const uint4 w = p[k];
+                    v[8 * k + 0] = bf16_lo(w.x); v[8 * k + 1] = bf16_hi(w.x);
+                    v[8 * k + 2] = bf16_lo(w.y); v[8 * k + 3] = bf16_hi(w.y);
+                    v[8 * k + 4] = bf16_lo(w.z); v[8 * k + 5] = bf16_hi(w.z);
+                    v[8 * k + 6] = bf16_lo(w.w); v[8 * k + 7] = bf16_hi(w.w);
+                }
             } else {
-                const float4 w = *(const float4*)((const float*)a.x + base);
-                v[i][0] = w.x; v[i][1] = w.y; v[i][2] = w.z; v[i][3] = w.w;
+                const float4* p = (const float4*)((const float*)a.x + base);
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    const float4 w = p[k];
+                    v[4 * k] = w.x; v[4 * k + 1] = w.y; v[4 * k + 2] = w.z; v[4 * k + 3] = w.w;
+                }
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < W; j++) {
-                float t = 0.0f;
-                if (i < nrow && j < ncol) {
-                    if constexpr (SRC == SRC_BF16) t = __uint_as_float((uint32_t)((const uint16_t*)a.x)[base + j] << 16);
-                    else t = ((const float*)a.x)[base + j];
+            for (int i = 0; i < 32; i++) v[i] = load1<SRC>(a.x, base + i);
+        }
+        if (a.two_level) {
+#pragma unroll
+            for (int i = 0; i < 32; i++) v[i] = div_ts(v[i], d);
+        }
+        uint32_t u[32];
+        if (a.sr) {
+            const uint64_t idx0 = (uint64_t)r * (uint64_t)a.cols + (uint64_t)(cb * 32);   // multiple of 32
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                const u32x4 w = philox_block((idx0 >> 2) + k, 0u, a.offset, a.k0, a.k1);
+                u[4 * k] = w.x; u[4 * k + 1] = w.y; u[4 * k + 2] = w.z; u[4 * k + 3] = w.w;
+            }
+        }
+        uint32_t codes[8];
+        const uint32_t sb = quantize_block<FMT>(v, a.hadamard, a.sr, u, codes);
+        store_codes<BITS>(a.q_row + r * (a.cols * BITS / 8) + cb * 32 * BITS / 8, codes);
+        a.s_row[r * nblk + cb] = (uint8_t)sb;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Column copy (and optionally the row copy) from an LDS-staged 64x128 tile.
+// ---------------------------------------------------------------------------
+template <int SRC, int FMT, bool ROW>
+__global__ __launch_bounds__(256) void k_quant_tile(QArgs a)
+{
+    constexpr int BITS = Fmt<FMT>::bits;
+    __shared__ __align__(16) float tile[TR * LDSW];
+    extern __shared__ __align__(16) uint32_t words[];  // SR: column-stream random words [TR][TC]
+
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.y * TR, c0 = (int64_t)blockIdx.x * TC;
+    const int nrow = (int)(a.rows - r0 < TR ? a.rows - r0 : TR);      // 32 or 64
+    const int ncol = (int)(a.cols - c0 < TC ? a.cols - c0 : TC);
+    const TensorDiv d = make_div(a.two_level ? *a.tscale : 1.0f);
+
+    // ---- stage the tile (zero outside the tensor), divided by s_t ----
+    constexpr int EPC = SRC == SRC_BF16 ? 8 : 4;      // elements per 16-byte chunk
+    constexpr int CPR = TC / EPC;                     // chunks per tile row
+#pragma unroll
+    for (int p = 0; p < TR * CPR / 256; p++) {
+        const int id = p * 256 + tid;
+        const int r = id / CPR, cc = (id % CPR) * EPC;
+        float v[EPC];
+        const int64_t base = (r0 + r) * a.ld + c0 + cc;
+        if (a.vec && r < nrow && cc + EPC <= ncol) {
+            const uint4 w = *(const uint4*)((const uint8_t*)a.x + base * (SRC == SRC_BF16 ? 2 : 4));
+            if constexpr (SRC == SRC_BF16) {
+                v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+                v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+            } else {
+                v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+                v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < EPC; k++) v[k] = (r < nrow && cc + k < ncol) ? load1<SRC>(a.x, base + k) : 0.0f;
+        }
+        if (a.two_level) {
+#pragma unroll
+            for (int k = 0; k < EPC; k++) v[k] = div_ts(v[k], d);
+        }
+#pragma unroll
+        for (int k = 0; k < EPC; k += 4)
+            *(float4*)&tile[r * LDSW + cc + k] = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+    }
+    // ---- column-stream Philox words for the tile (axis word 1) ----
+    if (a.sr) {
+        if ((a.cols & 3) == 0) {                       // 4 consecutive columns per call
+#pragma unroll 2
+            for (int p = 0; p < TR * TC / 4 / 256; p++) {
+                const int id = p * 256 + tid;
+                const int r = id / (TC / 4), c4 = (id % (TC / 4)) * 4;
+                if (r < nrow && c4 < ncol) {
+                    const uint64_t idx = (uint64_t)(r0 + r) * (uint64_t)a.cols + (uint64_t)(c0 + c4);
+                    const u32x4 w = philox_block(idx >> 2, 1u, a.offset, a.k0, a.k1);
+                    *(uint4*)&words[r * TC + c4] = make_uint4(w.x, w.y, w.z, w.w);
                 }
-                v[i][j] = t;
+            }
+        } else {                                       // general: one call per element
+            for (int p = 0; p < TR * TC / 256; p++) {
+                const int id = p * 256 + tid;
+                const int r = id / TC, c = id % TC;
+                if (r < nrow && c < ncol) {
+                    const uint64_t idx = (uint64_t)(r0 + r) * (uint64_t)a.cols + (uint64_t)(c0 + c);
+                    words[r * TC + c] = pick(philox_block(idx >> 2, 1u, a.offset, a.k0, a.k1), (uint32_t)(idx & 3));
+                }
             }
         }
     }
+    __syncthreads();
 
-    // ---- level 1 of the two-level scheme: x / s_t ----
-    if (a.two_level) {
-        const float st = load_tensor_scale<FMT>(a);
-#pragma unroll
-        for (int i = 0; i < 32; i++)
-#pragma unroll
-            for (int j = 0; j < W; j++) v[i][j] = v[i][j] / st;
-    }
-
-    // ---- row copy: 1x32 blocks spread over 8 lanes ----
+    // ---- row blocks: thread -> (row tid % 64, block tid / 64) ----
     if constexpr (ROW) {
-        const int64_t row_bytes = a.cols * BITS / 8;
-        const int64_t nblk = a.cols / 32;
+        const int r = tid % TR, blk = tid / TR;
+        if (r < nrow && blk * 32 < ncol) {
+            float v[32];
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
-            if (i >= nrow) continue;                     // wave-uniform
-            float t[W];
-#pragma unroll
-            for (int j = 0; j < W; j++) t[j] = v[i][j];
-            if (a.hadamard) {
-                // stages h = 1, 2 inside the lane, h = 4, 8, 16 across lanes
-#pragma unroll
-                for (int st = 0; st < 2; st++) {         // W = 4: h = 1, 2
-                    const int h = 1 << st;
-#pragma unroll
-                    for (int j = 0; j < W; j++)
-                        if ((j & h) == 0) {
-                            const float p = t[j], q = t[j + h];
-                            t[j] = p + q;
-                            t[j + h] = p - q;
-                        }
-                }
-#pragma unroll
-                for (int st = 0; st < 3; st++) {         // h = 4, 8, 16: lanes ^1, ^2, ^4
-                    const int m = 1 << st;
-#pragma unroll
-                    for (int j = 0; j < W; j++) {
-                        const float p = __shfl_xor(t[j], m);
-                        t[j] = (lane & m) ? (p - t[j]) : (t[j] + p);
-                    }
-                }
+            for (int k = 0; k < 8; k++) {
+                const float4 w = *(const float4*)&tile[r * LDSW + blk * 32 + 4 * k];
+                v[4 * k] = w.x; v[4 * k + 1] = w.y; v[4 * k + 2] = w.z; v[4 * k + 3] = w.w;
             }
-            uint32_t key = 0;
-#pragma unroll
-            for (int j = 0; j < W; j++) key = max(key, abs_key(t[j]));
-            key = max(key, (uint32_t)__shfl_xor((int)key, 1));
-            key = max(key, (uint32_t)__shfl_xor((int)key, 2));
-            key = max(key, (uint32_t)__shfl_xor((int)key, 4));
-            const bool finite = key < 0x7F800000u;
-            const int e = finite ? block_exponent<FMT>(key) : 0;
-            float y[W];
-#pragma unroll
-            for (int j = 0; j < W; j++) y[j] = scale_by(t[j], e);
+            uint32_t u[32];
             if (a.sr) {
-                const uint64_t idx = (uint64_t)(r0 + i) * (uint64_t)a.cols + (uint64_t)c0;
-                const u32x4 w = philox_block(idx >> 2, 0u, a.offset, a.k0, a.k1);  // cols % 4 == 0
-                y[0] = sr_value<FMT>(y[0], w.x); y[1] = sr_value<FMT>(y[1], w.y);
-                y[2] = sr_value<FMT>(y[2], w.z); y[3] = sr_value<FMT>(y[3], w.w);
-            } else {
+                const uint64_t idx0 = (uint64_t)(r0 + r) * (uint64_t)a.cols + (uint64_t)(c0 + blk * 32);
 #pragma unroll
-                for (int j = 0; j < W; j++) y[j] = clamp_fmax<FMT>(y[j]);
-            }
-            if (ncol == W) {
-                uint8_t* dst = a.q_row + (r0 + i) * row_bytes + c0 * BITS / 8;
-                if constexpr (BITS == 8) {
-                    uint32_t packed = cvt2_fp8<FMT>(y[0], y[1]) | (cvt2_fp8<FMT>(y[2], y[3]) << 16);
-                    if (!finite)
-                        packed = nan_code<FMT>(t[0]) | (nan_code<FMT>(t[1]) << 8) |
-                                 (nan_code<FMT>(t[2]) << 16) | (nan_code<FMT>(t[3]) << 24);
-                    *(uint32_t*)dst = packed;
-                } else {
-                    uint32_t packed = cvt2_fp4(y[0], y[1]) | (cvt2_fp4(y[2], y[3]) << 8);
-                    if (!finite) packed = 0;
-                    *(uint16_t*)dst = (uint16_t)packed;
+                for (int k = 0; k < 8; k++) {
+                    const u32x4 w = philox_block((idx0 >> 2) + k, 0u, a.offset, a.k0, a.k1);
+                    u[4 * k] = w.x; u[4 * k + 1] = w.y; u[4 * k + 2] = w.z; u[4 * k + 3] = w.w;
                 }
-                if ((lane & 7) == 0)
-                    a.s_row[(r0 + i) * nblk + c0 / 32] = (uint8_t)(finite ? e + 127 : 0xFF);
             }
+            uint32_t codes[8];
+            const uint32_t sb = quantize_block<FMT>(v, a.hadamard, a.sr, u, codes);
+            const int64_t gc = c0 + blk * 32;
+            store_codes<BITS>(a.q_row + (r0 + r) * (a.cols * BITS / 8) + gc * BITS / 8, codes);
+            a.s_row[(r0 + r) * (a.cols / 32) + gc / 32] = (uint8_t)sb;
         }
     }
 
-    // ---- column copy: 32x1 blocks inside the lane, stored transposed ----
-    if constexpr (COL) {
-        if (ncol == 0) return;
-        if (a.hadamard) {
+    // ---- column blocks: thread -> (column tid % 128, row block tid / 128) ----
+    {
+        const int c = tid % TC, rb = tid / TC;
+        if (c < ncol && rb * 32 < nrow) {
+            float v[32];
+            uint32_t u[32];
 #pragma unroll
-            for (int j = 0; j < W; j++) {
-                float col[32];
-#pragma unroll
-                for (int i = 0; i < 32; i++) col[i] = v[i][j];
-                fwht32(col);
-#pragma unroll
-                for (int i = 0; i < 32; i++) v[i][j] = col[i];
+            for (int i = 0; i < 32; i++) {
+                v[i] = tile[(rb * 32 + i) * LDSW + c];
+                u[i] = a.sr ? words[(rb * 32 + i) * TC + c] : 0u;
             }
-        }
-        int e[W];
-        bool finite[W];
-#pragma unroll
-        for (int j = 0; j < W; j++) {
-            uint32_t key = 0;
-#pragma unroll
-            for (int i = 0; i < 32; i++) key = max(key, abs_key(v[i][j]));
-            finite[j] = key < 0x7F800000u;
-            e[j] = finite[j] ? block_exponent<FMT>(key) : 0;
-        }
-        // codes of column j, element i at byte i (FP8) / nibble i (FP4)
-        constexpr int NW = BITS == 8 ? 8 : 4;           // dwords per column block
-        uint32_t code[W][NW];
-#pragma unroll
-        for (int j = 0; j < W; j++)
-#pragma unroll
-            for (int k = 0; k < NW; k++) code[j][k] = 0;
-        const bool fast_rng = (a.cols % 4) == 0;
-#pragma unroll
-        for (int i = 0; i < 32; i += 2) {
-            float y[2][W];
-#pragma unroll
-            for (int d = 0; d < 2; d++)
-#pragma unroll
-                for (int j = 0; j < W; j++) y[d][j] = scale_by(v[i + d][j], e[j]);
-            if (a.sr) {
-#pragma unroll
-                for (int d = 0; d < 2; d++) {
-                    const uint64_t idx = (uint64_t)(r0 + i + d) * (uint64_t)a.cols + (uint64_t)c0;
-                    if (fast_rng) {
-                        const u32x4 w = philox_block(idx >> 2, 1u, a.offset, a.k0, a.k1);
-                        y[d][0] = sr_value<FMT>(y[d][0], w.x); y[d][1] = sr_value<FMT>(y[d][1], w.y);
-                        y[d][2] = sr_value<FMT>(y[d][2], w.z); y[d][3] = sr_value<FMT>(y[d][3], w.w);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < W; j++) {
-                            const uint64_t ij = idx + j;
-                            const u32x4 w = philox_block(ij >> 2, 1u, a.offset, a.k0, a.k1);
-                            y[d][j] = sr_value<FMT>(y[d][j], pick(w, (uint32_t)(ij & 3)));
-                        }
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int d = 0; d < 2; d++)
-#pragma unroll
-                    for (int j = 0; j < W; j++) y[d][j] = clamp_fmax<FMT>(y[d][j]);
-            }
-#pragma unroll
-            for (int j = 0; j < W; j++) {
-                if constexpr (BITS == 8) {
-                    uint32_t c2 = cvt2_fp8<FMT>(y[0][j], y[1][j]);
-                    if (!finite[j]) c2 = nan_code<FMT>(v[i][j]) | (nan_code<FMT>(v[i + 1][j]) << 8);
-                    code[j][i / 4] |= c2 << (8 * (i % 4));
-                } else {
-                    uint32_t c2 = cvt2_fp4(y[0][j], y[1][j]);
-                    if (!finite[j]) c2 = 0;
-                    code[j][i / 8] |= c2 << (4 * (i % 8));
-                }
-            }
-        }
-        const int64_t col_bytes = a.rows * BITS / 8;
-        const int64_t nblk = a.rows / 32;
-#pragma unroll
-        for (int j = 0; j < W; j++) {
-            if (j < ncol) {
-                uint8_t* dst = a.q_col + (c0 + j) * col_bytes + r0 * BITS / 8;
-                *(uint4*)dst = make_uint4(code[j][0], code[j][1], code[j][2], code[j][3]);
-                if constexpr (BITS == 8)
-                    *(uint4*)(dst + 16) = make_uint4(code[j][4], code[j][5], code[j][6], code[j][7]);
-                a.s_col[(c0 + j) * nblk + r0 / 32] = (uint8_t)(finite[j] ? e[j] + 127 : 0xFF);
-            }
+            uint32_t codes[8];
+            const uint32_t sb = quantize_block<FMT>(v, a.hadamard, a.sr, u, codes);
+            const int64_t gc = c0 + c, gr = r0 + rb * 32;
+            store_codes<BITS>(a.q_col + gc * (a.rows * BITS / 8) + gr * BITS / 8, codes);
+            a.s_col[gc * (a.rows / 32) + gr / 32] = (uint8_t)sb;
         }
     }
 }
 
-// ---- level-1 tensor amax: |x| keys reduced with an integer max ----
-__global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
+// ---------------------------------------------------------------------------
+// Level-1 tensor amax (two-level scheme)
+// ---------------------------------------------------------------------------
+// max |x| key of the 8 (bf16) or 4 (fp32) elements of a 16-byte word
+template <int SRC>
+__device__ __forceinline__ uint32_t key16(uint4 w)
+{
+    if constexpr (SRC == SRC_BF16) {
+        const uint32_t m = max(max(max(w.x & 0x7FFFu, (w.x >> 16) & 0x7FFFu),
+                                   max(w.y & 0x7FFFu, (w.y >> 16) & 0x7FFFu)),
+                               max(max(w.z & 0x7FFFu, (w.z >> 16) & 0x7FFFu),
+                                   max(w.w & 0x7FFFu, (w.w >> 16) & 0x7FFFu)));
+        return m << 16;
+    } else {
+        return max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu));
+    }
+}
 
 template <int SRC>
-__global__ __launch_bounds__(256) void k_amax(const void* x, int64_t rows, int64_t cols,
-                                              int64_t ld, uint32_t* out)
+__device__ __forceinline__ uint32_t key1(const void* x, int64_t i)
 {
-    constexpr int W = 4;
-    const int64_t chunks_per_row = (cols + W - 1) / W;
-    const int64_t total = rows * chunks_per_row;
+    if constexpr (SRC == SRC_BF16) return ((uint32_t)((const uint16_t*)x)[i] << 16) & 0x7FFFFFFFu;
+    else return ((const uint32_t*)x)[i] & 0x7FFFFFFFu;
+}
+
+// Per-workgroup |x| keys (integer max: NaN keys exceed Inf, Inf exceeds every
+// finite value).  Dense 16-byte-aligned tensors are read as a flat run of
+// 16-byte words with several loads in flight; other layouts row by row.
+template <int SRC>
+__global__ __launch_bounds__(256) void k_amax_partial(const void* x, int64_t rows, int64_t cols,
+                                                      int64_t ld, int flat16, uint32_t* partial)
+{
     uint32_t key = 0;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-         t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = t / chunks_per_row;
-        const int64_t c = (t - r * chunks_per_row) * W;
-        const int64_t base = r * ld + c;
-        if (c + W <= cols) {
-            if constexpr (SRC == SRC_BF16) {
-                const uint2 w = *(const uint2*)((const uint16_t*)x + base);
-                key = max(key, max(max(w.x & 0x7FFFu, (w.x >> 16) & 0x7FFFu),
-                                   max(w.y & 0x7FFFu, (w.y >> 16) & 0x7FFFu)) << 16);
-            } else {
-                const uint4 w = *(const uint4*)((const float*)x + base);
-                key = max(key, max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu),
-                                   max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu)));
-            }
-        } else {
-            for (int64_t j = c; j < cols; j++) {
-                uint32_t b;
-                if constexpr (SRC == SRC_BF16) b = (uint32_t)((const uint16_t*)x)[r * ld + j] << 16;
-                else b = ((const uint32_t*)x)[r * ld + j];
-                key = max(key, b & 0x7FFFFFFFu);
-            }
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (flat16) {
+        constexpr int EPW = SRC == SRC_BF16 ? 8 : 4;
+        const int64_t nw = rows * cols / EPW;            // whole 16-byte words
+        const uint4* p = (const uint4*)x;
+        int64_t i = t0;
+        for (; i + 7 * stride < nw; i += 8 * stride) {   // eight loads in flight
+            uint4 w[8];
+#pragma unroll
+            for (int k = 0; k < 8; k++) w[k] = p[i + k * stride];
+#pragma unroll
+            for (int k = 0; k < 8; k++) key = max(key, key16<SRC>(w[k]));
         }
+        for (; i < nw; i += stride) key = max(key, key16<SRC>(p[i]));
+        for (int64_t e = nw * EPW + t0; e < rows * cols; e += stride) key = max(key, key1<SRC>(x, e));
+    } else {
+        for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
+            for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) key = max(key, key1<SRC>(x, r * ld + c));
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
     __shared__ uint32_t red[4];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = key;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t k = max(max(red[0], red[1]), max(red[2], red[3]));
-        atomicMax(out, k);
-    }
+    if (threadIdx.x == 0) partial[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
+// One workgroup: s_t from the partial keys, written to the tensor-scale word
+// (which may itself hold the single partial of a tiny tensor).
 template <int FMT>
-__global__ void k_tscale_finalize(float* ts)
+__global__ __launch_bounds__(256) void k_amax_reduce(const uint32_t* partial, int n, float* ts)
 {
-    const uint32_t key = *(const uint32_t*)ts;
-    *ts = tensor_scale_from_key<FMT>(key);
+    uint32_t key = 0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) key = max(key, partial[i]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
+    __shared__ uint32_t red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = key;
+    __syncthreads();
+    if (threadIdx.x == 0) *ts = tensor_scale_from_key<FMT>(max(max(red[0], red[1]), max(red[2], red[3])));
 }
 
 template <int SRC, int FMT>
@@ -337,22 +407,40 @@ hipError_t launch_fmt(const QuantJob& j, hipStream_t stream)
     a.tscale = j.tensor_scale;
     a.k0 = (uint32_t)j.seed; a.k1 = (uint32_t)(j.seed >> 32); a.offset = j.offset;
     a.sr = j.sr; a.hadamard = j.hadamard; a.two_level = j.two_level;
+    const int es = j.src == SRC_BF16 ? 2 : 4;
+    a.vec = ((reinterpret_cast<uintptr_t>(j.x) & 15u) == 0) && ((j.ld * es) % 16 == 0);
 
     if (j.two_level == 1) {
-        uint32_t* word = (uint32_t*)j.tensor_scale;
-        k_fill_u32<<<1, 1, 0, stream>>>(word, 0u);
-        const int64_t chunks = j.rows * ((j.cols + 3) / 4);
-        int64_t blocks = (chunks + 255) / 256;
-        if (blocks > 1024) blocks = 1024;
-        k_amax<SRC><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(j.x, j.rows, j.cols, j.ld, word);
+        // partial keys parked in the scale array this call overwrites later
+        uint8_t* sbuf = j.s_row ? j.s_row : j.s_col;
+        const int64_t sbytes = j.s_row ? j.rows * (j.cols / 32) : j.cols * (j.rows / 32);
+        const uintptr_t pad = (4 - (reinterpret_cast<uintptr_t>(sbuf) & 3u)) & 3u;
+        int64_t cap = (sbytes - (int64_t)pad) / 4;
+        const int flat16 = a.vec && j.ld == j.cols;
+        const int64_t words = j.rows * j.cols * es / 16;
+        int64_t want = flat16 ? (words + 2047) / 2048 : j.rows;
+        want = want < 1 ? 1 : (want > 512 ? 512 : want);
+        uint32_t* partial = (uint32_t*)(sbuf + pad);
+        int64_t n = want < cap ? want : cap;
+        if (n < 1) {                       // tiny tensor: the tensor-scale word holds the key
+            n = 1;
+            partial = (uint32_t*)j.tensor_scale;
+        }
+        k_amax_partial<SRC><<<dim3((unsigned)n), dim3(256), 0, stream>>>(j.x, j.rows, j.cols, j.ld, flat16, partial);
+        k_amax_reduce<FMT><<<dim3(1), dim3(256), 0, stream>>>(partial, (int)n, j.tensor_scale);
     }
-    const dim3 grid((unsigned)((j.cols + 64 * kSubW - 1) / (64 * kSubW)),
-                    (unsigned)((j.rows + 32 * kWaves - 1) / (32 * kWaves)));
-    const dim3 block(256);
-    if (j.q_row && j.q_col) k_quant<SRC, FMT, true, true><<<grid, block, 0, stream>>>(a);
-    else if (j.q_row) k_quant<SRC, FMT, true, false><<<grid, block, 0, stream>>>(a);
-    else k_quant<SRC, FMT, false, true><<<grid, block, 0, stream>>>(a);
-    if (j.two_level == 1) k_tscale_finalize<FMT><<<1, 1, 0, stream>>>(j.tensor_scale);
+    if (j.q_col) {
+        const dim3 grid((unsigned)((j.cols + TC - 1) / TC), (unsigned)((j.rows + TR - 1) / TR));
+        const size_t dyn = j.sr ? (size_t)TR * TC * sizeof(uint32_t) : 0;
+        if (j.q_row) k_quant_tile<SRC, FMT, true><<<grid, dim3(256), dyn, stream>>>(a);
+        else k_quant_tile<SRC, FMT, false><<<grid, dim3(256), dyn, stream>>>(a);
+    } else {
+        const int64_t nblk = j.cols / 32;
+        int64_t gy = (j.rows + 3) / 4;
+        gy = gy > 65535 ? 65535 : gy;
+        const dim3 grid((unsigned)((nblk + 63) / 64), (unsigned)gy);
+        k_quant_row<SRC, FMT><<<grid, dim3(256), 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

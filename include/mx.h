@@ -97,7 +97,8 @@ typedef struct {
  *      fp32, stages 1,2,4,8,16);
  *   3. e = floor(log2(max|v|)) - emax(fmt), clamped to [-127,127] (-127
  *      for an all-zero block); scale byte = e + 127; a block holding a
- *      NaN or Inf gets byte 0xFF and NaN codes (E2M1: 0);
+ *      NaN or Inf gets byte 0xFF and every element the code 0x7F (the
+ *      format's NaN; E2M1, which has none: 0);
  *   4. y = v * 2^-e (exact); RNE, or SR: with lo <= |y| < hi the
  *      neighbouring codes and F = floor((|y|-lo)/(hi-lo) * 2^32), round up
  *      iff u < F, where u is word (idx & 3) of Philox4x32-10 with counter
@@ -105,14 +106,16 @@ typedef struct {
  *      and idx = r*cols + c the element's row-major index in the source;
  *      |y| >= Fmax saturates to +-Fmax; the sign is kept (also for zero).
  *
- * x:     source, `src_dtype`, rows x cols with row stride `ld` elements;
- *        16-byte aligned, ld*elem_size a multiple of 16, ld >= cols.
+ * x:     source, `src_dtype`, rows x cols with row stride `ld` elements,
+ *        ld >= cols, aligned to the element size.  (16-byte aligned x with
+ *        ld*elem_size a multiple of 16 takes the vector-load path.)
  * rows, cols: > 0.  MX_AXIS_ROW needs cols % 32 == 0; MX_AXIS_COL needs
  *        rows % 32 == 0.
  * q, scales: the stored copy (layouts above); q 16-byte aligned.
  * tensor_scale: one fp32 in device memory.  Two-level + COMPUTE: written
- *        with s_t (used as scratch while the amax is reduced, so it must
- *        not be read before the stream reaches the end of this call).
+ *        with s_t.  While the amax is reduced, the scale array (and, for a
+ *        tiny tensor, this word) holds partial maxima, so neither may be
+ *        read before the stream reaches the end of this call.
  *        Two-level + PROVIDED: read.  MX_SCALE_E8M0: ignored (may be NULL).
  * Errors: MX_ERR_INVALID_ARG (null pointers, block != 32, bad enum,
  *        reserved != 0, shapes above), MX_ERR_ALIGNMENT, MX_ERR_HIP.

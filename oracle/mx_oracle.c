@@ -96,11 +96,14 @@ int or_emax(int fmt) { return ilogb(or_fmax(fmt)); }
 
 static unsigned nan_code(int fmt, int negative)
 {
-    /* FP8 formats: the all-ones magnitude is a NaN in E4M3 and E5M2.
+    /* FP8 formats: the all-ones magnitude 0x7F is a NaN in E4M3 and E5M2.
      * E2M1 has no NaN: such elements are written as +0 (their block's
-     * scale byte 0xFF already marks the block as NaN). */
+     * scale byte 0xFF already marks the block as NaN).  The sign is not
+     * used: IEEE 754 leaves the sign of a NaN produced by arithmetic (for
+     * instance by the Hadamard) unspecified, so the code must not carry it. */
+    (void)negative;
     if (fmt == OR_E2M1) return 0u;
-    return (negative ? 0x80u : 0u) | 0x7Fu;
+    return 0x7Fu;
 }
 
 /* index i with t[i] <= a < t[i+1]; requires 0 <= a < fmax */

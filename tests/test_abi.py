@@ -58,8 +58,8 @@ def _q(lib, x=FAKE, src=1, rows=64, cols=64, ld=64, axis=0, cfg=None, q=FAKE, s=
     (dict(axis=2), mx.MX_ERR_INVALID_ARG),
     (dict(cols=48, ld=48), mx.MX_ERR_INVALID_ARG),              # row blocks need cols % 32
     (dict(axis=1, rows=40), mx.MX_ERR_INVALID_ARG),             # col blocks need rows % 32
-    (dict(x=FAKE_ODD), mx.MX_ERR_ALIGNMENT),
-    (dict(ld=68), mx.MX_ERR_ALIGNMENT),                         # 68 * 2 bytes not 16-aligned
+    (dict(x=FAKE + 1), mx.MX_ERR_ALIGNMENT),                   # bf16 source on an odd address
+    (dict(x=FAKE + 2, src=0), mx.MX_ERR_ALIGNMENT),            # fp32 source not 4-byte aligned
     (dict(q=FAKE_ODD), mx.MX_ERR_ALIGNMENT),
 ])
 def test_quantize_validation(lib, kw, status):

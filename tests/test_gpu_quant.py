@@ -250,3 +250,26 @@ def test_full_llama3_8b_mlp_dual_sampled():
         _sampled_compare(x, (qr, sr_), O.AXIS_ROW, fmt, 1500, rng)
         _sampled_compare(x, (qc, sc), O.AXIS_COL, fmt, 1500, rng)
         log("mlp", name, "ok")
+
+
+@pytest.mark.parametrize("st", [0.0371, 1.0, 3.0, float.fromhex("0x1.fffffep-1"),
+                                float.fromhex("0x1.555556p-2"), 2.0 ** -60,
+                                float.fromhex("0x1.3b8f3ep+5"), 1e-30])
+def test_two_level_division_every_bf16(st):
+    """The tensor-scale division inside the quantizer on every finite bf16
+    value (both signs) and a wide fp32 sample, with provided scales:
+    codes must equal the oracle's, whose step is the IEEE fp32 division."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint16)
+    allv = np.concatenate([bits, bits | 0x8000]).astype(np.uint16)
+    pad = (-allv.size) % 1024
+    x = np.concatenate([allv, np.zeros(pad, np.uint16)]).reshape(-1, 1024)
+    rng = np.random.default_rng(8)
+    xf = (rng.standard_normal((256, 1024)) * np.exp2(rng.uniform(-120, 120, (256, 1024)))).astype(np.float32)
+    ts = torch.tensor([st], dtype=torch.float32, device=DEV)
+    for src in (x, xf):
+        for fmt in ("e4m3", "e2m1"):
+            cfg = mx.qconfig(fmt, two_level=True, tscale_provided=True)
+            q, s, _ = mx.mx_quantize(to_device(src), mx.MX_AXIS_ROW, cfg, tensor_scale=ts)
+            qo, so, _ = O.quantize(src, O.AXIS_ROW, fmt, two_level=2, tensor_scale=float(np.float32(st)))
+            assert_codes_equal(u8(q), qo, f"{fmt} st={st} codes")
+            assert_codes_equal(u8(s), so, f"{fmt} st={st} scales")

@@ -180,7 +180,8 @@ def test_nonfinite_block_reading():
     for fmt in (O.E4M3, O.E5M2):
         q, s, _ = O.quantize(x, O.AXIS_ROW, fmt)
         assert s[0, 0] == 0xFF and s[1, 0] == 0xFF
-        assert q[0, 0] == 0x7F and q[1, 4] == 0xFF and q[1, 5] == 0xFF
+        # every element of a non-finite block: the canonical NaN, no sign
+        assert np.all(q[0] == 0x7F) and np.all(q[1] == 0x7F)
     q, s, _ = O.quantize(x, O.AXIS_ROW, O.E2M1)
     assert s[0, 0] == 0xFF and not q.any()
 
