@@ -195,7 +195,8 @@ def main():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="moss", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-flush", action="store_true")
+    p.add_argument("--flush", default="write", choices=["write", "read", "none"],
+                   help="how L2/MALL are evicted before each step (outside the timed kernels)")
     args = p.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: this build has no multi-GPU path "
@@ -205,11 +206,13 @@ def main():
     mx.load()
     log(f"workload {args.workload}: generating inputs")
     step, info = WORKLOADS[args.workload](args)
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = None if args.flush == "none" else torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
 
     def one(t):
-        if flush is not None:
+        if args.flush == "write":
             flush.zero_()
+        elif args.flush == "read":
+            flush.max()
         step(t)
 
     warm = Timer()
@@ -261,7 +264,9 @@ def main():
            "data": "synthetic (seeded; no weights or datasets)",
            "config": info["config"], "roofline": roofline,
            "kernels": quant, "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
-           "timing": "HIP events on the launch stream; L2/MALL flushed before each step (not timed)"}
+           "timing": "HIP events on the launch stream; L2/MALL evicted before each step by a 512 MiB "
+                     f"{args.flush} (not timed)" if flush is not None else
+                     "HIP events on the launch stream; no cache eviction between steps"}
     if info["gemm_kernel"]:
         out["kernels"]["gemm"] = {"ms": round(kernel_ms[info["gemm_kernel"]], 4),
                                   "TFLOP/s": roofline["achieved"], "frac_mfma": roofline["frac"]}

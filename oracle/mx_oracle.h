@@ -11,8 +11,8 @@
  *          for memory efficient FP8 Training" (dignews.cc)
  *   [FAF]  "格式感知融合:让FP4预训练提速两倍的工程实践" (kongchang.com)
  * Element formats and the shared-scale rule follow the OCP Microscaling
- * (MX) Formats specification v1.0, which the pages name ("the MX standard")
- * but do not restate.
+ * (MX) Formats specification v1.0, which the pages refer to by name but do
+ * not restate.
  */
 #ifndef MX_ORACLE_H
 #define MX_ORACLE_H
