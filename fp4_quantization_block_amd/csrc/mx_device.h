@@ -78,20 +78,29 @@ __device__ __forceinline__ float clamp_fmax(float y)
     return __builtin_amdgcn_fmed3f(y, -Fmt<FMT>::fmax, Fmt<FMT>::fmax);
 }
 
-// two FP8 codes (y0 -> low byte, y1 -> high byte) of a 16-bit lane
+// four FP8 codes (y0 lowest byte ... y3 highest) in one dword: the converter
+// writes a 16-bit half of its destination and keeps the other half.
 template <int FMT>
-__device__ __forceinline__ uint32_t cvt2_fp8(float y0, float y1)
+__device__ __forceinline__ uint32_t cvt4_fp8(float y0, float y1, float y2, float y3)
 {
-    if constexpr (FMT == E4M3)
-        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false) & 0xFFFFu;
-    else
-        return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(y0, y1, 0, false) & 0xFFFFu;
+    if constexpr (FMT == E4M3) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, lo, true);
+    } else {
+        const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(y0, y1, 0, false);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(y2, y3, lo, true);
+    }
 }
 
-// two FP4 codes (y0 -> low nibble, y1 -> high nibble) of a byte
-__device__ __forceinline__ uint32_t cvt2_fp4(float y0, float y1)
+// eight FP4 codes in one dword (element 2j in the low nibble of byte j): the
+// converter writes one byte of its destination and keeps the others.  The
+// scale operand is 1.0, i.e. the values are already scaled.
+__device__ __forceinline__ uint32_t cvt8_fp4(const float* y)
 {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0) & 0xFFu;
+    uint32_t d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, y[2], y[3], 1.0f, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, y[4], y[5], 1.0f, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, y[6], y[7], 1.0f, 3);
 }
 
 // ---------------------------------------------------------------------
@@ -132,9 +141,10 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 {
 #pragma unroll
     for (int r = 0; r < 10; r++) {
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
-        c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+        // one 32x32->64 product gives both halves (a single v_mad_u64_u32)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+        c = u32x4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0};
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }

@@ -17,14 +17,18 @@
 //   k_quant_row   row copy only: one thread per 1x32 block, read straight
 //                 from global memory (64 contiguous bytes per lane for bf16),
 //                 no cross-lane traffic.
-//   k_quant_tile  column copy, or both copies from one read: a 256-thread
-//                 workgroup stages a 64-row x 128-column tile in LDS (rows
-//                 padded to keep the two access patterns bank-conflict free),
-//                 then each thread quantizes one 1x32 row block and/or one
-//                 32x1 column block.  Column copies are stored transposed.
-//                 For stochastic rounding of column blocks the workgroup
-//                 first generates the tile's Philox words cooperatively into
-//                 LDS, one 4-word block per call, so no word is wasted.
+//   k_quant_tile_dma / k_quant_tile_reg   column copy, or both copies from
+//                 one read.  Persistent workgroups walk 128-row x 64-column
+//                 tiles held raw in LDS; each of 256 compute threads then
+//                 quantizes one 1x32 row block and one 32x1 column block.
+//                 Column copies are stored transposed, a 128-byte run per
+//                 column and tile.  The _dma form (16-byte-aligned sources)
+//                 adds a loader wave that streams the next tile straight into
+//                 a second LDS buffer while the current one is quantized; the
+//                 _reg form prefetches into registers and handles any
+//                 alignment.  For stochastic rounding of column blocks the
+//                 workgroup generates the tile's Philox words into LDS, four
+//                 per call, so no word is wasted.
 //   k_amax_partial / k_amax_reduce   level-1 tensor amax for the two-level
 //                 scheme: per-workgroup partial maxima, then one workgroup
 //                 writes s_t = amax / Fmax.  The partials are parked in the
@@ -37,8 +41,14 @@ namespace mx {
 
 namespace {
 
-constexpr int TR = 64, TC = 128;           // tile of k_quant_tile
-constexpr int LDSW = TC + 4;               // padded LDS row (floats)
+constexpr int TR = 128, TC = 64;           // quantizer tile (rows x columns)
+
+template <int SRC> struct SrcT;
+template <> struct SrcT<SRC_BF16> { static constexpr int bytes = 2; };
+template <> struct SrcT<SRC_F32> { static constexpr int bytes = 4; };
+
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct QArgs {
     const void* x;
@@ -47,8 +57,9 @@ struct QArgs {
     uint8_t* q_col; uint8_t* s_col;
     const float* tscale;          // s_t (two-level), read by the quantize kernels
     uint32_t k0, k1, offset;
-    int sr, hadamard, two_level;
+    int hadamard, two_level;
     int vec;                      // 1: x and every row start are 16-byte aligned
+    int64_t ntx, ntiles;          // tiles per tile row, tile count
 };
 
 // FP32 tensor scale s_t = amax / Fmax (IEEE division); 1 for an all-zero
@@ -64,68 +75,130 @@ __device__ __forceinline__ float tensor_scale_from_key(uint32_t key)
 // x / s_t rounded to nearest even, with s_t fixed for the whole tensor.  The
 // reciprocal r = RN(1/s_t) is formed once; q = RN(x r) refined by one exact
 // residual step q' = RN(q + RN(x - q s_t) r) equals the IEEE quotient
-// whenever |x|, |q'| >= 2^-96 and |q'| <= 2^17 (the quantizer has |x| <= amax =
-// Fmax s_t, so |x / s_t| <= 57344); other operands, zeros included, take the
-// IEEE division.  (Checked exhaustively over every fp32 x for a set of
-// divisors with adversarial significands.)
+// whenever |x|, |q'| >= 2^-96 and |q'| <= 2^17 (checked exhaustively over
+// every fp32 x for a set of divisors with adversarial significands).  Per
+// block the kernels check |x| >= T = max(2^-96, 2^-95 |s_t|) for every
+// nonzero x (which implies |q'| >= 2^-96) and |q'| <= 2^17 on the block's
+// largest quotient; a block that fails takes the IEEE division.  Zeros keep
+// the sign of x r; a non-finite x makes the block non-finite either way.
 struct TensorDiv {
     float s, r;
-    bool fast;      // s and 1/s are normal fp32 numbers
+    uint32_t lo_key;    // (bits(T) << 1) - 1
+    bool fast;          // s and 1/s are normal fp32 numbers
 };
 
 __device__ __forceinline__ TensorDiv make_div(float s)
 {
+    TensorDiv d;
     const float as = fabsf(s);
-    return TensorDiv{s, 1.0f / s, as > 0x1p-125f && as < 0x1p125f};
+    d.s = s;
+    d.r = 1.0f / s;
+    d.fast = as > 0x1p-125f && as < 0x1p125f;
+    const float t = d.fast ? fmaxf(0x1p-96f, 0x1p-95f * as) : 1.0f;
+    d.lo_key = (__float_as_uint(t) << 1) - 1u;
+    return d;
 }
 
-__device__ __forceinline__ float div_ts(float x, const TensorDiv& d)
+// fast quotient; `lo` tracks min((bits(x) << 1) - 1), whose value is below
+// lo_key exactly when some nonzero |x| < T
+__device__ __forceinline__ float div_fast(float x, const TensorDiv& d, uint32_t& lo)
 {
-    if (!d.fast) return x / d.s;
-    float q = x * d.r;
-    const float rem = __builtin_fmaf(-q, d.s, x);
-    q = __builtin_fmaf(rem, d.r, q);
-    if (!(fabsf(q) >= 0x1p-96f && fabsf(q) <= 0x1p17f) || fabsf(x) < 0x1p-96f) q = x / d.s;
-    return q;
+    const float q0 = x * d.r;
+    const float rem = __builtin_fmaf(-q0, d.s, x);
+    const float q1 = __builtin_fmaf(rem, d.r, q0);
+    lo = min(lo, (__float_as_uint(x) << 1) - 1u);
+    return __builtin_copysignf(q1, q0);
 }
 
-// Quantizes one 32-element block v (already divided by s_t, Hadamard not yet
-// applied).  u[i]: the element's random word (SR only).  Writes 8 (FP8) or 4
-// (FP4) packed dwords of codes; returns the scale byte.  A block holding a
-// NaN or Inf gets byte 0xFF and the format's canonical NaN code 0x7F for
-// every element (E2M1, which has no NaN: 0) -- the sign of a NaN produced by
-// arithmetic is not defined by IEEE 754, so no sign is carried.
-template <int FMT>
-__device__ __forceinline__ uint32_t quantize_block(float (&v)[32], bool had, bool sr,
-                                                   const uint32_t* u, uint32_t* out)
+// The 32 values of one block ready for the block scale: source values from
+// elem(i), divided by s_t (two-level) and transformed (Hadamard).  Returns the
+// block's |max| key.
+template <class Elem>
+__device__ __forceinline__ uint32_t block_values(Elem&& elem, bool two_level, bool had,
+                                                 const TensorDiv& d, float (&v)[32])
+{
+#pragma unroll
+    for (int i = 0; i < 32; i++) v[i] = elem(i);
+    uint32_t key = 0;
+    bool have = false;
+    if (two_level) {
+        bool slow = !d.fast;
+        if (d.fast) {
+            uint32_t lo = ~0u, qk = 0;
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                v[i] = div_fast(v[i], d, lo);
+                qk = max(qk, abs_key(v[i]));
+            }
+            slow = lo < d.lo_key || (qk > 0x48000000u && qk < 0x7F800000u);   // 0x48000000 = 2^17
+            key = qk;
+        }
+        if (slow) {
+            key = 0;
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                v[i] = elem(i) / d.s;
+                key = max(key, abs_key(v[i]));
+            }
+        }
+        have = true;
+    }
+    if (had) {
+        fwht32(v);
+        have = false;
+    }
+    if (!have) {
+        key = 0;
+#pragma unroll
+        for (int i = 0; i < 32; i++) key = max(key, abs_key(v[i]));
+    }
+    return key;
+}
+
+// |max| key of 32 bf16 values held as 16 packed dwords (packed 16-bit max)
+__device__ __forceinline__ uint32_t bf16_block_key(const uint32_t* w)
+{
+    ushort2v m = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 16; j++) m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2v, w[j] & 0x7FFF7FFFu));
+    return (uint32_t)max(m.x, m.y) << 16;
+}
+
+// Encodes one block whose 32 values v have the |max| key `key`.  words(k)
+// returns the random words of elements 4k..4k+3 (SR only).  Writes 8 (FP8)
+// or 4 (FP4) dwords of packed codes; returns the scale byte.  A block
+// holding a NaN or Inf gets byte 0xFF and the canonical NaN code 0x7F for
+// every element (E2M1, which has no NaN: 0) -- IEEE 754 leaves the sign of a
+// NaN produced by arithmetic undefined, so no sign is carried.
+template <int FMT, bool SR, class Words>
+__device__ __forceinline__ uint32_t encode_block(const float (&v)[32], uint32_t key, Words&& words,
+                                                 uint32_t* out)
 {
     constexpr int BITS = Fmt<FMT>::bits;
-    if (had) fwht32(v);
-    uint32_t key = 0;
-#pragma unroll
-    for (int i = 0; i < 32; i++) key = max(key, abs_key(v[i]));
     if (key >= 0x7F800000u) {
-        constexpr uint32_t fill = BITS == 8 ? 0x7F7F7F7Fu : 0u;
 #pragma unroll
-        for (int k = 0; k < (BITS == 8 ? 8 : 4); k++) out[k] = fill;
+        for (int k = 0; k < (BITS == 8 ? 8 : 4); k++) out[k] = BITS == 8 ? 0x7F7F7F7Fu : 0u;
         return 0xFFu;
     }
     const int e = block_exponent<FMT>(key);
     float y[32];
 #pragma unroll
-    for (int i = 0; i < 32; i++) {
-        const float t = scale_by(v[i], e);
-        y[i] = sr ? sr_value<FMT>(t, u[i]) : clamp_fmax<FMT>(t);
+    for (int k = 0; k < 8; k++) {
+        u32x4 w{0u, 0u, 0u, 0u};
+        if constexpr (SR) w = words(k);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float t = scale_by(v[4 * k + j], e);
+            y[4 * k + j] = SR ? sr_value<FMT>(t, u[j]) : clamp_fmax<FMT>(t);
+        }
     }
     if constexpr (BITS == 8) {
 #pragma unroll
-        for (int k = 0; k < 8; k++)
-            out[k] = cvt2_fp8<FMT>(y[4 * k], y[4 * k + 1]) | (cvt2_fp8<FMT>(y[4 * k + 2], y[4 * k + 3]) << 16);
+        for (int k = 0; k < 8; k++) out[k] = cvt4_fp8<FMT>(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]);
     } else {
 #pragma unroll
-        for (int k = 0; k < 4; k++)
-            out[k] = cvt2_fp4(y[8 * k], y[8 * k + 1]) | (cvt2_fp4(y[8 * k + 2], y[8 * k + 3]) << 8) |
-                     (cvt2_fp4(y[8 * k + 4], y[8 * k + 5]) << 16) | (cvt2_fp4(y[8 * k + 6], y[8 * k + 7]) << 24);
+        for (int k = 0; k < 4; k++) out[k] = cvt8_fp4(&y[8 * k]);
     }
     return (uint32_t)(e + 127);
 }
@@ -137,21 +210,40 @@ __device__ __forceinline__ void store_codes(uint8_t* dst, const uint32_t* w)
     if constexpr (BITS == 8) *(uint4*)(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
+// raw bits of source element i (bf16 in the low 16 bits)
 template <int SRC>
-__device__ __forceinline__ float load1(const void* x, int64_t i)
+__device__ __forceinline__ uint32_t raw1(const void* x, int64_t i)
 {
-    if constexpr (SRC == SRC_BF16) return __uint_as_float((uint32_t)((const uint16_t*)x)[i] << 16);
-    else return ((const float*)x)[i];
+    if constexpr (SRC == SRC_BF16) return ((const uint16_t*)x)[i];
+    else return ((const uint32_t*)x)[i];
 }
+
+// source value from a raw dword array: element i of bf16 pairs or fp32 words
+template <int SRC>
+__device__ __forceinline__ float unpack(const uint32_t* w, int i)
+{
+    if constexpr (SRC == SRC_BF16) return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+    else return __uint_as_float(w[i]);
+}
+
+// the four row-stream (axis 0) words of elements 4(n0 + k) .. 4(n0 + k) + 3
+struct RowWords {
+    uint64_t n0; uint32_t offset, k0, k1;
+    __device__ __forceinline__ u32x4 operator()(int k) const
+    {
+        return philox_block(n0 + (uint64_t)k, 0u, offset, k0, k1);
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Row copy: one thread per 1x32 block.  Grid: x covers the blocks of a row
 // in runs of 64 (one per lane), y covers rows four at a time (one per wave).
 // ---------------------------------------------------------------------------
-template <int SRC, int FMT>
+template <int SRC, int FMT, bool SR>
 __global__ __launch_bounds__(256) void k_quant_row(QArgs a)
 {
     constexpr int BITS = Fmt<FMT>::bits;
+    constexpr int NW = SRC == SRC_BF16 ? 16 : 32;      // source dwords per block
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t nblk = a.cols / 32;
     const int64_t cb = (int64_t)blockIdx.x * 64 + lane;
@@ -159,100 +251,74 @@ __global__ __launch_bounds__(256) void k_quant_row(QArgs a)
     const TensorDiv d = make_div(a.two_level ? *a.tscale : 1.0f);
     for (int64_t r = (int64_t)blockIdx.y * 4 + wave; r < a.rows; r += (int64_t)gridDim.y * 4) {
         const int64_t base = r * a.ld + cb * 32;
-        float v[32];
+        uint32_t w[NW];
         if (a.vec) {
-            if constexpr (SRC == SRC_BF16) {
-                const uint4* p = (const uint4*)((const uint16_t*)a.x + base);
+            const uint4* p = (const uint4*)((const uint8_t*)a.x + base * SrcT<SRC>::bytes);
 #pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const uint4 w = p[k];
-                    v[8 * k + 0] = bf16_lo(w.x); v[8 * k + 1] = bf16_hi(w.x);
-                    v[8 * k + 2] = bf16_lo(w.y); v[8 * k + 3] = bf16_hi(w.y);
-                    v[8 * k + 4] = bf16_lo(w.z); v[8 * k + 5] = bf16_hi(w.z);
-                    v[8 * k + 6] = bf16_lo(w.w); v[8 * k + 7] = bf16_hi(w.w);
-                }
-            } else {
-                const float4* p = (const float4*)((const float*)a.x + base);
-#pragma unroll
-                for (int k = 0; k < 8; k++) {
-                    const float4 w = p[k];
-                    v[4 * k] = w.x; v[4 * k + 1] = w.y; v[4 * k + 2] = w.z; v[4 * k + 3] = w.w;
-                }
+            for (int k = 0; k < NW / 4; k++) {
+                const uint4 t = p[k];
+                w[4 * k] = t.x; w[4 * k + 1] = t.y; w[4 * k + 2] = t.z; w[4 * k + 3] = t.w;
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 32; i++) v[i] = load1<SRC>(a.x, base + i);
+            for (int j = 0; j < NW; j++)
+                w[j] = SRC == SRC_BF16 ? raw1<SRC>(a.x, base + 2 * j) | (raw1<SRC>(a.x, base + 2 * j + 1) << 16)
+                                       : raw1<SRC>(a.x, base + j);
         }
-        if (a.two_level) {
+        float v[32];
+        uint32_t key;
+        if (SRC == SRC_BF16 && !a.two_level && !a.hadamard) {
 #pragma unroll
-            for (int i = 0; i < 32; i++) v[i] = div_ts(v[i], d);
+            for (int i = 0; i < 32; i++) v[i] = unpack<SRC>(w, i);
+            key = bf16_block_key(w);
+        } else {
+            key = block_values([&](int i) { return unpack<SRC>(w, i); }, a.two_level, a.hadamard, d, v);
         }
-        uint32_t u[32];
-        if (a.sr) {
-            const uint64_t idx0 = (uint64_t)r * (uint64_t)a.cols + (uint64_t)(cb * 32);   // multiple of 32
-#pragma unroll
-            for (int k = 0; k < 8; k++) {
-                const u32x4 w = philox_block((idx0 >> 2) + k, 0u, a.offset, a.k0, a.k1);
-                u[4 * k] = w.x; u[4 * k + 1] = w.y; u[4 * k + 2] = w.z; u[4 * k + 3] = w.w;
-            }
-        }
+        const RowWords words{((uint64_t)r * (uint64_t)a.cols + (uint64_t)(cb * 32)) >> 2, a.offset, a.k0, a.k1};
         uint32_t codes[8];
-        const uint32_t sb = quantize_block<FMT>(v, a.hadamard, a.sr, u, codes);
+        const uint32_t sb = encode_block<FMT, SR>(v, key, words, codes);
         store_codes<BITS>(a.q_row + r * (a.cols * BITS / 8) + cb * 32 * BITS / 8, codes);
         a.s_row[r * nblk + cb] = (uint8_t)sb;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Column copy (and optionally the row copy) from an LDS-staged 64x128 tile.
+// Column copy (and optionally the row copy) through LDS-staged tiles of
+// TR x TC source elements.  Two LDS layouts of a tile:
+//   PadLayout  rows padded by 16 bytes (tiles written from registers);
+//   SwzLayout  dense rows whose 16-byte chunks are XOR-permuted by a key of
+//              the row (tiles written by direct global->LDS loads, which fill
+//              1 KiB of consecutive LDS per instruction).
+// Both keep the row-block reads (16 consecutive rows, ds_read_b128) and the
+// column reads (64 consecutive columns of one row) free of bank conflicts.
 // ---------------------------------------------------------------------------
-template <int SRC, int FMT, bool ROW>
-__global__ __launch_bounds__(256) void k_quant_tile(QArgs a)
-{
-    constexpr int BITS = Fmt<FMT>::bits;
-    __shared__ __align__(16) float tile[TR * LDSW];
-    extern __shared__ __align__(16) uint32_t words[];  // SR: column-stream random words [TR][TC]
-
-    const int tid = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.y * TR, c0 = (int64_t)blockIdx.x * TC;
-    const int nrow = (int)(a.rows - r0 < TR ? a.rows - r0 : TR);      // 32 or 64
-    const int ncol = (int)(a.cols - c0 < TC ? a.cols - c0 : TC);
-    const TensorDiv d = make_div(a.two_level ? *a.tscale : 1.0f);
-
-    // ---- stage the tile (zero outside the tensor), divided by s_t ----
-    constexpr int EPC = SRC == SRC_BF16 ? 8 : 4;      // elements per 16-byte chunk
-    constexpr int CPR = TC / EPC;                     // chunks per tile row
-#pragma unroll
-    for (int p = 0; p < TR * CPR / 256; p++) {
-        const int id = p * 256 + tid;
-        const int r = id / CPR, cc = (id % CPR) * EPC;
-        float v[EPC];
-        const int64_t base = (r0 + r) * a.ld + c0 + cc;
-        if (a.vec && r < nrow && cc + EPC <= ncol) {
-            const uint4 w = *(const uint4*)((const uint8_t*)a.x + base * (SRC == SRC_BF16 ? 2 : 4));
-            if constexpr (SRC == SRC_BF16) {
-                v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-                v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-            } else {
-                v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
-                v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < EPC; k++) v[k] = (r < nrow && cc + k < ncol) ? load1<SRC>(a.x, base + k) : 0.0f;
-        }
-        if (a.two_level) {
-#pragma unroll
-            for (int k = 0; k < EPC; k++) v[k] = div_ts(v[k], d);
-        }
-#pragma unroll
-        for (int k = 0; k < EPC; k += 4)
-            *(float4*)&tile[r * LDSW + cc + k] = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+template <int SRC> struct PadLayout {
+    static constexpr int RB = TC * SrcT<SRC>::bytes, PITCH = RB + 16, BYTES = TR * PITCH;
+    __device__ static int at(int row, int byte) { return row * PITCH + byte; }
+};
+template <int SRC> struct SwzLayout {
+    static constexpr int RB = TC * SrcT<SRC>::bytes, BYTES = TR * RB;
+    __device__ static int key(int row) { return SRC == SRC_BF16 ? (row >> 1) & 7 : row & 15; }
+    __device__ static int at(int row, int byte)
+    {
+        return row * RB + ((((byte >> 4) ^ key(row)) << 4) | (byte & 15));
     }
-    // ---- column-stream Philox words for the tile (axis word 1) ----
-    if (a.sr) {
-        if ((a.cols & 3) == 0) {                       // 4 consecutive columns per call
-#pragma unroll 2
+};
+
+// Quantizes the tile at (r0, c0) held in LDS: one row block (ROW) and one
+// column block per thread of the 256 compute threads; for SR the column words
+// are generated into `words` first.  words_ready() is the workgroup barrier
+// between generating and reading them.
+template <int SRC, int FMT, bool ROW, bool SR, class L, class Sync>
+__device__ __forceinline__ void quantize_tile(const QArgs& a, const TensorDiv& d, const uint8_t* tile,
+                                              uint32_t* words, int64_t r0, int64_t c0, int nrow, int ncol,
+                                              int tid, Sync&& words_ready)
+{
+    constexpr int EB = SrcT<SRC>::bytes;
+    constexpr int BITS = Fmt<FMT>::bits;
+    if constexpr (SR) {
+        if ((a.cols & 3) == 0) {                // one call per 4 consecutive columns
+#pragma unroll
             for (int p = 0; p < TR * TC / 4 / 256; p++) {
                 const int id = p * 256 + tid;
                 const int r = id / (TC / 4), c4 = (id % (TC / 4)) * 4;
@@ -262,7 +328,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(QArgs a)
                     *(uint4*)&words[r * TC + c4] = make_uint4(w.x, w.y, w.z, w.w);
                 }
             }
-        } else {                                       // general: one call per element
+        } else {                                // general: one call per element
             for (int p = 0; p < TR * TC / 256; p++) {
                 const int id = p * 256 + tid;
                 const int r = id / TC, c = id % TC;
@@ -273,52 +339,364 @@ __global__ __launch_bounds__(256) void k_quant_tile(QArgs a)
             }
         }
     }
-    __syncthreads();
 
-    // ---- row blocks: thread -> (row tid % 64, block tid / 64) ----
+    // ---- row block: thread -> (row tid % 128, block tid / 128) ----
     if constexpr (ROW) {
-        const int r = tid % TR, blk = tid / TR;
-        if (r < nrow && blk * 32 < ncol) {
+        const int r = tid % TR, h = tid / TR;
+        if (r < nrow && h * 32 < ncol) {
+            constexpr int NW = 32 * EB / 4;
+            uint32_t w[NW];
+#pragma unroll
+            for (int k = 0; k < NW / 4; k++) {
+                const uint4 q = *(const uint4*)&tile[L::at(r, h * 32 * EB + 16 * k)];
+                w[4 * k] = q.x; w[4 * k + 1] = q.y; w[4 * k + 2] = q.z; w[4 * k + 3] = q.w;
+            }
             float v[32];
+            uint32_t key;
+            if (SRC == SRC_BF16 && !a.two_level && !a.hadamard) {
 #pragma unroll
-            for (int k = 0; k < 8; k++) {
-                const float4 w = *(const float4*)&tile[r * LDSW + blk * 32 + 4 * k];
-                v[4 * k] = w.x; v[4 * k + 1] = w.y; v[4 * k + 2] = w.z; v[4 * k + 3] = w.w;
+                for (int i = 0; i < 32; i++) v[i] = unpack<SRC>(w, i);
+                key = bf16_block_key(w);
+            } else {
+                key = block_values([&](int i) { return unpack<SRC>(w, i); }, a.two_level, a.hadamard, d, v);
             }
-            uint32_t u[32];
-            if (a.sr) {
-                const uint64_t idx0 = (uint64_t)(r0 + r) * (uint64_t)a.cols + (uint64_t)(c0 + blk * 32);
-#pragma unroll
-                for (int k = 0; k < 8; k++) {
-                    const u32x4 w = philox_block((idx0 >> 2) + k, 0u, a.offset, a.k0, a.k1);
-                    u[4 * k] = w.x; u[4 * k + 1] = w.y; u[4 * k + 2] = w.z; u[4 * k + 3] = w.w;
-                }
-            }
+            const int64_t gc = c0 + h * 32;
+            const RowWords rw{((uint64_t)(r0 + r) * (uint64_t)a.cols + (uint64_t)gc) >> 2, a.offset, a.k0, a.k1};
             uint32_t codes[8];
-            const uint32_t sb = quantize_block<FMT>(v, a.hadamard, a.sr, u, codes);
-            const int64_t gc = c0 + blk * 32;
+            const uint32_t sb = encode_block<FMT, SR>(v, key, rw, codes);
             store_codes<BITS>(a.q_row + (r0 + r) * (a.cols * BITS / 8) + gc * BITS / 8, codes);
             a.s_row[(r0 + r) * (a.cols / 32) + gc / 32] = (uint8_t)sb;
         }
     }
+    if constexpr (SR) words_ready();
 
-    // ---- column blocks: thread -> (column tid % 128, row block tid / 128) ----
-    {
-        const int c = tid % TC, rb = tid / TC;
-        if (c < ncol && rb * 32 < nrow) {
-            float v[32];
-            uint32_t u[32];
-#pragma unroll
-            for (int i = 0; i < 32; i++) {
-                v[i] = tile[(rb * 32 + i) * LDSW + c];
-                u[i] = a.sr ? words[(rb * 32 + i) * TC + c] : 0u;
-            }
-            uint32_t codes[8];
-            const uint32_t sb = quantize_block<FMT>(v, a.hadamard, a.sr, u, codes);
-            const int64_t gc = c0 + c, gr = r0 + rb * 32;
-            store_codes<BITS>(a.q_col + gc * (a.rows * BITS / 8) + gr * BITS / 8, codes);
-            a.s_col[gc * (a.rows / 32) + gr / 32] = (uint8_t)sb;
+    // ---- column block: thread -> (column tid % 64, row block tid / 64) ----
+    const int c = tid % TC, rb = tid / TC;
+    if (c < ncol && rb * 32 < nrow) {
+        auto elem = [&](int i) {
+            const uint8_t* p = &tile[L::at(rb * 32 + i, c * EB)];
+            if constexpr (SRC == SRC_BF16) return __uint_as_float((uint32_t)*(const uint16_t*)p << 16);
+            else return *(const float*)p;
+        };
+        float v[32];
+        const uint32_t key = block_values(elem, a.two_level, a.hadamard, d, v);
+        auto cw = [&](int k) {
+            const uint32_t* p = &words[(rb * 32 + 4 * k) * TC + c];
+            return u32x4{p[0], p[TC], p[2 * TC], p[3 * TC]};
+        };
+        uint32_t codes[8];
+        const uint32_t sb = encode_block<FMT, SR>(v, key, cw, codes);
+        const int64_t gc = c0 + c, gr = r0 + rb * 32;
+        store_codes<BITS>(a.q_col + gc * (a.rows * BITS / 8) + gr * BITS / 8, codes);
+        a.s_col[gc * (a.rows / 32) + gr / 32] = (uint8_t)sb;
+    }
+}
+
+// The k-th tile (TRR x TCC) of this workgroup's sequence ((r0, c0) of its
+// corner), or false past the end.  Workgroups are dealt to the 8 XCDs
+// round-robin; when the grid allows, XCD j walks its own strip of tile
+// columns (row-major inside the strip), so the partial lines of both output
+// copies -- a row's code and scale bytes, a column's scale bytes -- are
+// completed inside one XCD's L2 instead of being merged in memory.
+template <int TRR, int TCC>
+__device__ __forceinline__ bool tile_at(const QArgs& a, int64_t k, int64_t& r0, int64_t& c0)
+{
+    const int64_t nty = a.ntiles / a.ntx;
+    if (a.ntx >= 8 && (gridDim.x & 7) == 0) {
+        const int64_t j = blockIdx.x & 7, l = blockIdx.x >> 3, L = gridDim.x >> 3;
+        const int64_t x0 = j * a.ntx / 8, x1 = (j + 1) * a.ntx / 8, width = x1 - x0;
+        const int64_t s = l + k * L;
+        if (s >= width * nty) return false;
+        r0 = (s / width) * TRR;
+        c0 = (x0 + s % width) * TCC;
+        return true;
+    }
+    const int64_t t = blockIdx.x + k * (int64_t)gridDim.x;
+    if (t >= a.ntiles) return false;
+    r0 = (t / a.ntx) * TRR;
+    c0 = (t % a.ntx) * TCC;
+    return true;
+}
+
+template <int TRR, int TCC>
+__device__ __forceinline__ void tile_extent(const QArgs& a, int64_t r0, int64_t c0, int& nrow, int& ncol)
+{
+    nrow = (int)(a.rows - r0 < TRR ? a.rows - r0 : TRR);      // a multiple of 32
+    ncol = (int)(a.cols - c0 < TCC ? a.cols - c0 : TCC);
+}
+
+// Barrier for LDS hand-offs without a memory fence: waits only for this
+// wave's LDS traffic (not for its global stores), then s_barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Same for the loader wave: its direct-to-LDS loads have landed.
+__device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// k_quant_tile_dma: 16-byte-aligned sources, round to nearest.  Tiles of
+// 128 rows x 256 source bytes (128 bf16 or 64 fp32 columns).  NCW compute
+// waves plus one loader wave: the loader streams the next tile straight into
+// the other LDS buffer (direct global->LDS buffer loads, one 256-byte tile row
+// per instruction; rows past the tensor read as zero, columns past it hold
+// neighbouring data, and neither is used) while the compute waves quantize
+// the current one, so the compute waves never wait on a global load and the
+// loader never waits on a store.  Codes are staged back into the tile's own
+// LDS buffer once every block has been read, then written out as whole runs:
+// each column's codes for the tile form one 128-byte (FP8) or 64-byte (FP4)
+// run of the transposed copy, each row's one run of the row copy, and scale
+// bytes leave four to a store.  Scattered 16- to 32-byte stores (one per
+// block) were measured at under 2.2 TB/s on this part; whole runs reach the
+// HBM rate.
+// ---------------------------------------------------------------------------
+template <int SRC> struct DmaTile {
+    static constexpr int EB = SrcT<SRC>::bytes, ROWS = 128, COLS = 256 / EB, RB = 256;
+    // rows padded by 16 bytes: 16 consecutive rows read with ds_read_b128
+    // start in 16 different bank groups; a row read by consecutive lanes is
+    // contiguous
+    static constexpr int PITCH = RB + 16, BYTES = ROWS * PITCH;
+    // compute waves: one column block and one row block per thread for bf16
+    static constexpr int NCW = SRC == SRC_BF16 ? 8 : 4;
+    __device__ static int at(int row, int byte) { return row * PITCH + byte; }
+};
+
+// Output staging of LB-byte lines (LB = 32, 64 or 128): the 16-byte chunks of
+// a line are XOR-permuted so that 16 lanes writing one chunk of 16
+// consecutive lines, or reading consecutive chunks, hit distinct banks.
+template <int LB>
+__device__ __forceinline__ int stage_at(int line, int chunk)
+{
+    constexpr int CH = LB / 16, LPR = 256 / LB;
+    return line * LB + ((chunk ^ ((line / LPR) % CH)) << 4);
+}
+
+// n scale bytes (n <= 4) from a staged dword to dst: one store when aligned
+__device__ __forceinline__ void store_scales(uint8_t* dst, uint32_t w, int n)
+{
+    if (n == 4 && (reinterpret_cast<uintptr_t>(dst) & 3u) == 0) {
+        *(uint32_t*)dst = w;
+    } else if (n == 2 && (reinterpret_cast<uintptr_t>(dst) & 1u) == 0) {
+        *(uint16_t*)dst = (uint16_t)w;
+    } else {
+        for (int i = 0; i < n; i++) dst[i] = (uint8_t)(w >> (8 * i));
+    }
+}
+
+template <int SRC, int FMT, bool ROW>
+__global__ __launch_bounds__(64 * (DmaTile<SRC>::NCW + 1)) void k_quant_tile_dma(QArgs a)
+{
+    using T = DmaTile<SRC>;
+    constexpr int EB = T::EB, TRR = T::ROWS, TCC = T::COLS, NCT = 64 * T::NCW;
+    constexpr int BITS = Fmt<FMT>::bits, CW = BITS == 8 ? 8 : 4;   // code dwords per block
+    constexpr int LBC = TRR * BITS / 8;         // bytes of one column's codes per tile
+    constexpr int LBR = TCC * BITS / 8;         // bytes of one row's codes per tile
+    constexpr int NT = TRR * TCC / 32 / NCT;    // column (and row) blocks per compute thread
+    constexpr int SPR = TCC / 32;               // row scale bytes per tile row
+    static_assert(NT >= 1 && TRR * TCC / 32 == NT * NCT, "tile / thread split");
+    static_assert(TCC * LBC + TRR * LBR <= T::BYTES, "staging fits the tile buffer");
+    __shared__ __align__(16) uint8_t buf0[T::BYTES];
+    __shared__ __align__(16) uint8_t buf1[T::BYTES];
+    __shared__ __align__(4) uint8_t sc_col[TCC * 4];
+    __shared__ __align__(4) uint8_t sc_row[TRR * SPR];
+
+    const int tid = threadIdx.x;
+    if (tid >= NCT) {
+        // ---------------- loader wave ----------------
+        const uint32_t voff = (uint32_t)(4 * (tid - NCT));
+        auto issue = [&](int64_t r0, int64_t c0, uint8_t* dst) {
+            int64_t n = ((a.rows - r0 - 1) * a.ld + (a.cols - c0)) * EB;
+            n = n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n;
+            const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)((const uint8_t*)a.x + (r0 * a.ld + c0) * EB), (short)0, (int)(uint32_t)n, 0x00020000);
+            const uint32_t row_bytes = (uint32_t)(a.ld * EB);
+#pragma unroll 8
+            for (int j = 0; j < TRR; j++)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + j * T::PITCH), 4, voff,
+                                                         j * row_bytes, 0, 0);
+        };
+        int64_t r0, c0;
+        if (tile_at<TRR, TCC>(a, 0, r0, c0)) issue(r0, c0, buf0);
+        dma_barrier();
+        for (int64_t k = 0; tile_at<TRR, TCC>(a, k, r0, c0); k++) {
+            int64_t r1, c1;
+            if (tile_at<TRR, TCC>(a, k + 1, r1, c1)) issue(r1, c1, (k & 1) ? buf0 : buf1);
+            lds_barrier();                                // compute: tile read
+            lds_barrier();                                // compute: codes staged
+            dma_barrier();                                // end of tile
         }
+        return;
+    }
+    // ---------------- compute waves ----------------
+    const TensorDiv d = make_div(a.two_level ? *a.tscale : 1.0f);
+    const auto none = [](int) { return u32x4{0u, 0u, 0u, 0u}; };
+    lds_barrier();
+    int64_t r0, c0;
+    for (int64_t k = 0; tile_at<TRR, TCC>(a, k, r0, c0); k++) {
+        uint8_t* tile = (k & 1) ? buf1 : buf0;
+        int nrow, ncol;
+        tile_extent<TRR, TCC>(a, r0, c0, nrow, ncol);
+        uint32_t ccode[NT][CW], csc[NT], rcode[NT][CW], rsc[NT];
+
+        // column blocks: q -> (column q % TCC, row block q / TCC)
+#pragma unroll
+        for (int j = 0; j < NT; j++) {
+            const int q = tid + NCT * j, c = q % TCC, rb = q / TCC;
+            if (c < ncol && rb * 32 < nrow) {
+                auto elem = [&](int i) {
+                    const uint8_t* p = &tile[T::at(rb * 32 + i, c * EB)];
+                    if constexpr (SRC == SRC_BF16) return __uint_as_float((uint32_t)*(const uint16_t*)p << 16);
+                    else return *(const float*)p;
+                };
+                float v[32];
+                const uint32_t key = block_values(elem, a.two_level, a.hadamard, d, v);
+                csc[j] = encode_block<FMT, false>(v, key, none, ccode[j]);
+            }
+        }
+        // row blocks: q -> (row q % TRR, block q / TRR)
+        if constexpr (ROW) {
+#pragma unroll
+            for (int j = 0; j < NT; j++) {
+                const int q = tid + NCT * j, r = q % TRR, blk = q / TRR;
+                if (r < nrow && blk * 32 < ncol) {
+                    constexpr int NW = 32 * EB / 4;
+                    uint32_t w[NW];
+#pragma unroll
+                    for (int m = 0; m < NW / 4; m++) {
+                        const uint4 t4 = *(const uint4*)&tile[T::at(r, blk * 32 * EB + 16 * m)];
+                        w[4 * m] = t4.x; w[4 * m + 1] = t4.y; w[4 * m + 2] = t4.z; w[4 * m + 3] = t4.w;
+                    }
+                    float v[32];
+                    uint32_t key;
+                    if (SRC == SRC_BF16 && !a.two_level && !a.hadamard) {
+#pragma unroll
+                        for (int i = 0; i < 32; i++) v[i] = unpack<SRC>(w, i);
+                        key = bf16_block_key(w);
+                    } else {
+                        key = block_values([&](int i) { return unpack<SRC>(w, i); }, a.two_level, a.hadamard, d, v);
+                    }
+                    rsc[j] = encode_block<FMT, false>(v, key, none, rcode[j]);
+                }
+            }
+        }
+        lds_barrier();                                   // every block of the tile has been read
+
+        // stage codes and scales (column runs first, then row runs)
+        uint8_t* scol = tile;
+        uint8_t* srow = tile + TCC * LBC;
+#pragma unroll
+        for (int j = 0; j < NT; j++) {
+            const int q = tid + NCT * j, c = q % TCC, rb = q / TCC;
+            if (c < ncol && rb * 32 < nrow) {
+#pragma unroll
+                for (int m = 0; m < CW / 4; m++)
+                    *(uint4*)&scol[stage_at<LBC>(c, rb * (CW / 4) + m)] =
+                        make_uint4(ccode[j][4 * m], ccode[j][4 * m + 1], ccode[j][4 * m + 2], ccode[j][4 * m + 3]);
+                sc_col[c * 4 + rb] = (uint8_t)csc[j];
+            }
+        }
+        if constexpr (ROW) {
+#pragma unroll
+            for (int j = 0; j < NT; j++) {
+                const int q = tid + NCT * j, r = q % TRR, blk = q / TRR;
+                if (r < nrow && blk * 32 < ncol) {
+#pragma unroll
+                    for (int m = 0; m < CW / 4; m++)
+                        *(uint4*)&srow[stage_at<LBR>(r, blk * (CW / 4) + m)] =
+                            make_uint4(rcode[j][4 * m], rcode[j][4 * m + 1], rcode[j][4 * m + 2], rcode[j][4 * m + 3]);
+                    sc_row[r * SPR + blk] = (uint8_t)rsc[j];
+                }
+            }
+        }
+        lds_barrier();                                   // staging complete
+
+        // whole runs out
+        const int64_t colbytes = a.rows * BITS / 8, rowbytes = a.cols * BITS / 8;
+        for (int id = tid; id < TCC * (LBC / 16); id += NCT) {
+            const int line = id / (LBC / 16), ch = id % (LBC / 16);
+            if (line < ncol && ch * 16 < nrow * BITS / 8)
+                *(uint4*)(a.q_col + (c0 + line) * colbytes + r0 * BITS / 8 + ch * 16) =
+                    *(const uint4*)&scol[stage_at<LBC>(line, ch)];
+        }
+        if constexpr (ROW) {
+            for (int id = tid; id < TRR * (LBR / 16); id += NCT) {
+                const int line = id / (LBR / 16), ch = id % (LBR / 16);
+                if (line < nrow && ch * 16 < ncol * BITS / 8)
+                    *(uint4*)(a.q_row + (r0 + line) * rowbytes + c0 * BITS / 8 + ch * 16) =
+                        *(const uint4*)&srow[stage_at<LBR>(line, ch)];
+            }
+        }
+        if (tid < ncol)
+            store_scales(a.s_col + (c0 + tid) * (a.rows / 32) + r0 / 32, *(const uint32_t*)&sc_col[tid * 4], nrow / 32);
+        if constexpr (ROW) {
+            const int r = tid - (NCT - TRR);                 // the last TRR compute threads
+            if (r >= 0 && r < nrow) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int i = 0; i < SPR; i++) w |= (uint32_t)sc_row[r * SPR + i] << (8 * i);
+                store_scales(a.s_row + (r0 + r) * (a.cols / 32) + c0 / 32, w, ncol / 32);
+            }
+        }
+        lds_barrier();                                   // tile buffer free for the loader
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_quant_tile_reg: any alignment.  Persistent workgroups; the next tile is
+// loaded into registers (element by element where needed) while the current
+// one is quantized, then written to a padded LDS tile.
+// ---------------------------------------------------------------------------
+template <int SRC, int FMT, bool ROW, bool SR>
+__global__ __launch_bounds__(256) void k_quant_tile_reg(QArgs a)
+{
+    using L = PadLayout<SRC>;
+    constexpr int EB = SrcT<SRC>::bytes;
+    constexpr int CPR = L::RB / 16;             // 16-byte chunks per tile row
+    constexpr int NLD = TR * CPR / 256;         // chunks per thread
+    constexpr int EPC = 16 / EB;                // elements per chunk
+    __shared__ __align__(16) uint8_t tile[L::BYTES];
+    extern __shared__ __align__(16) uint32_t words[];
+
+    const int tid = threadIdx.x;
+    const TensorDiv d = make_div(a.two_level ? *a.tscale : 1.0f);
+    uint4 pre[NLD];
+
+    auto load = [&](int64_t r0, int64_t c0) {
+        int nrow, ncol;
+        tile_extent<TR, TC>(a, r0, c0, nrow, ncol);
+#pragma unroll
+        for (int p = 0; p < NLD; p++) {
+            const int id = p * 256 + tid;
+            const int r = id / CPR, cc = (id % CPR) * EPC;
+            const int64_t e0 = (r0 + r) * a.ld + c0 + cc;
+            if (a.vec && r < nrow && cc + EPC <= ncol) {
+                pre[p] = *(const uint4*)((const uint8_t*)a.x + e0 * EB);
+            } else {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int k = 0; k < EPC; k++)
+                    if (r < nrow && cc + k < ncol) {
+                        if constexpr (SRC == SRC_BF16) w[k >> 1] |= raw1<SRC>(a.x, e0 + k) << (16 * (k & 1));
+                        else w[k] = raw1<SRC>(a.x, e0 + k);
+                    }
+                pre[p] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    };
+
+    int64_t r0, c0;
+    if (tile_at<TR, TC>(a, 0, r0, c0)) load(r0, c0);
+    for (int64_t k = 0; tile_at<TR, TC>(a, k, r0, c0); k++) {
+#pragma unroll
+        for (int p = 0; p < NLD; p++) {
+            const int id = p * 256 + tid;
+            *(uint4*)&tile[L::at(id / CPR, (id % CPR) * 16)] = pre[p];
+        }
+        int nrow, ncol;
+        tile_extent<TR, TC>(a, r0, c0, nrow, ncol);
+        __syncthreads();
+        int64_t r1, c1;
+        if (tile_at<TR, TC>(a, k + 1, r1, c1)) load(r1, c1);      // in flight while this tile is quantized
+        quantize_tile<SRC, FMT, ROW, SR, L>(a, d, tile, words, r0, c0, nrow, ncol, tid,
+                                            [] { __syncthreads(); });
+        __syncthreads();                                  // tile (and words) free for the next tile
     }
 }
 
@@ -398,6 +776,40 @@ __global__ __launch_bounds__(256) void k_amax_reduce(const uint32_t* partial, in
     if (threadIdx.x == 0) *ts = tensor_scale_from_key<FMT>(max(max(red[0], red[1]), max(red[2], red[3])));
 }
 
+// persistent grid: as many workgroups as stay resident together (at most 4
+// per CU), never more than there are tiles
+template <int SRC, int FMT, bool ROW, bool SR>
+hipError_t launch_tile(QArgs a, hipStream_t stream)
+{
+    // direct loads address a tile's rows with 32-bit offsets from its first
+    // row; stochastic rounding (bound by its Philox arithmetic) stays on the
+    // register-fed kernel, whose tile also holds the column words
+    const bool dma = !SR && a.vec != 0 && a.ld * SrcT<SRC>::bytes * 128 < (int64_t(1) << 32);
+    const size_t dyn = SR ? (size_t)TR * TC * sizeof(uint32_t) : 0;
+    const int tcols = dma ? DmaTile<SRC>::COLS : TC, trows = dma ? DmaTile<SRC>::ROWS : TR;
+    a.ntx = (a.cols + tcols - 1) / tcols;
+    a.ntiles = a.ntx * ((a.rows + trows - 1) / trows);
+    const void* fn = dma ? reinterpret_cast<const void*>(&k_quant_tile_dma<SRC, FMT, ROW>)
+                         : reinterpret_cast<const void*>(&k_quant_tile_reg<SRC, FMT, ROW, SR>);
+    const int threads = dma ? 64 * (DmaTile<SRC>::NCW + 1) : 256;
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, dyn);
+    if (e != hipSuccess) return e;
+    per_cu = per_cu < 1 ? 1 : (per_cu > 4 ? 4 : per_cu);
+    int64_t grid = (int64_t)cus * per_cu;
+    grid = grid < a.ntiles ? grid : a.ntiles;
+    if constexpr (!SR) {
+        if (dma) {
+            k_quant_tile_dma<SRC, FMT, ROW><<<dim3((unsigned)grid), dim3(threads), 0, stream>>>(a);
+            return hipGetLastError();
+        }
+    }
+    k_quant_tile_reg<SRC, FMT, ROW, SR><<<dim3((unsigned)grid), dim3(256), dyn, stream>>>(a);
+    return hipGetLastError();
+}
+
 template <int SRC, int FMT>
 hipError_t launch_fmt(const QuantJob& j, hipStream_t stream)
 {
@@ -406,19 +818,20 @@ hipError_t launch_fmt(const QuantJob& j, hipStream_t stream)
     a.q_row = j.q_row; a.s_row = j.s_row; a.q_col = j.q_col; a.s_col = j.s_col;
     a.tscale = j.tensor_scale;
     a.k0 = (uint32_t)j.seed; a.k1 = (uint32_t)(j.seed >> 32); a.offset = j.offset;
-    a.sr = j.sr; a.hadamard = j.hadamard; a.two_level = j.two_level;
+    a.hadamard = j.hadamard; a.two_level = j.two_level;
     const int es = j.src == SRC_BF16 ? 2 : 4;
     a.vec = ((reinterpret_cast<uintptr_t>(j.x) & 15u) == 0) && ((j.ld * es) % 16 == 0);
+    a.ntx = a.ntiles = 0;                 // set by the tile launcher
 
     if (j.two_level == 1) {
         // partial keys parked in the scale array this call overwrites later
         uint8_t* sbuf = j.s_row ? j.s_row : j.s_col;
         const int64_t sbytes = j.s_row ? j.rows * (j.cols / 32) : j.cols * (j.rows / 32);
         const uintptr_t pad = (4 - (reinterpret_cast<uintptr_t>(sbuf) & 3u)) & 3u;
-        int64_t cap = (sbytes - (int64_t)pad) / 4;
+        const int64_t cap = (sbytes - (int64_t)pad) / 4;
         const int flat16 = a.vec && j.ld == j.cols;
-        const int64_t words = j.rows * j.cols * es / 16;
-        int64_t want = flat16 ? (words + 2047) / 2048 : j.rows;
+        const int64_t nwords = j.rows * j.cols * es / 16;
+        int64_t want = flat16 ? (nwords + 2047) / 2048 : j.rows;
         want = want < 1 ? 1 : (want > 512 ? 512 : want);
         uint32_t* partial = (uint32_t*)(sbuf + pad);
         int64_t n = want < cap ? want : cap;
@@ -430,17 +843,15 @@ hipError_t launch_fmt(const QuantJob& j, hipStream_t stream)
         k_amax_reduce<FMT><<<dim3(1), dim3(256), 0, stream>>>(partial, (int)n, j.tensor_scale);
     }
     if (j.q_col) {
-        const dim3 grid((unsigned)((j.cols + TC - 1) / TC), (unsigned)((j.rows + TR - 1) / TR));
-        const size_t dyn = j.sr ? (size_t)TR * TC * sizeof(uint32_t) : 0;
-        if (j.q_row) k_quant_tile<SRC, FMT, true><<<grid, dim3(256), dyn, stream>>>(a);
-        else k_quant_tile<SRC, FMT, false><<<grid, dim3(256), dyn, stream>>>(a);
-    } else {
-        const int64_t nblk = j.cols / 32;
-        int64_t gy = (j.rows + 3) / 4;
-        gy = gy > 65535 ? 65535 : gy;
-        const dim3 grid((unsigned)((nblk + 63) / 64), (unsigned)gy);
-        k_quant_row<SRC, FMT><<<grid, dim3(256), 0, stream>>>(a);
+        if (j.q_row) return j.sr ? launch_tile<SRC, FMT, true, true>(a, stream) : launch_tile<SRC, FMT, true, false>(a, stream);
+        return j.sr ? launch_tile<SRC, FMT, false, true>(a, stream) : launch_tile<SRC, FMT, false, false>(a, stream);
     }
+    const int64_t nblk = j.cols / 32;
+    int64_t gy = (j.rows + 3) / 4;
+    gy = gy > 65535 ? 65535 : gy;
+    const dim3 grid((unsigned)((nblk + 63) / 64), (unsigned)gy);
+    if (j.sr) k_quant_row<SRC, FMT, true><<<grid, dim3(256), 0, stream>>>(a);
+    else k_quant_row<SRC, FMT, false><<<grid, dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
