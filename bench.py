@@ -8,7 +8,7 @@ two-level workload (M = N = K = 4096, A bf16 Student-t(3) activations with
   2. mx_quantize(B [K][N], column copy -> [N][K], same format)
   3. mx_gemm(A, B) with the tensor scales applied once in the epilogue,
      bf16 output.
-Inputs are resident in HBM before timing starts; a 512 MiB write evicts
+Inputs are resident in HBM before timing starts; a 512 MiB read evicts
 L2/MALL before every step (outside the timed kernels) so no step reads its
 inputs from cache.  Kernel times come from HIP events recorded on the stream
 the kernels run on.
@@ -33,6 +33,16 @@ from fp4_quantization_block_amd import mx  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0}   # dense scaled MFMA
+
+# HBM-side bytes per launch of the roofline kernel, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch) scaled by what the same
+# counters read for a 512 MiB device copy (x2.0 and x1.0); the summary and
+# commands are in profiles/.  Keyed by the SHA-256 of the kernel's source
+# file at measurement time: a changed kernel reports null until re-measured.
+MEASURED_TRAFFIC = {
+    "moss": {"source": "gemm.hip", "sha256": "4e3958dda526f895",
+             "fetch_kib": 51013.2, "write_kib": 32768.0},
+}
 
 
 def log(*a):
@@ -188,6 +198,20 @@ def cpu_baseline_moss(host, rows_sample=256):
                       f"0..{rows_sample - 1} of {M} ({t2 - t1:.2f} s, scaled x{M // rows_sample})"}
 
 
+def measured_traffic(workload):
+    """Bytes per launch of the roofline kernel if the counters match the
+    current kernel source, else None."""
+    import hashlib
+    m = MEASURED_TRAFFIC.get(workload)
+    if m is None:
+        return None
+    src = os.path.join(ROOT, "fp4_quantization_block_amd", "csrc", m["source"])
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if digest != m["sha256"]:
+        return None
+    return int(round(m["fetch_kib"] * 1024 * 2.0 + m["write_kib"] * 1024 * 1.0))
+
+
 def main():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -195,8 +219,10 @@ def main():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="moss", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--flush", default="write", choices=["write", "read", "none"],
-                   help="how L2/MALL are evicted before each step (outside the timed kernels)")
+    p.add_argument("--flush", default="read", choices=["write", "read", "none"],
+                   help="how L2/MALL are evicted before each step (outside the timed kernels); a "
+                        "512 MiB write leaves the caches full of dirty lines whose write-back then "
+                        "lands in the first timed kernel, so the default evicts by reading")
     args = p.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: this build has no multi-GPU path "
@@ -242,7 +268,7 @@ def main():
         g_tf = info["flops"] / (g_ms * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[info["mfma"]]
         roofline = {"bound": "mfma", "achieved": round(g_tf, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(g_tf / peak, 4), "traffic": None,
+                    "frac": round(g_tf / peak, 4), "traffic": measured_traffic(args.workload),
                     "kernel": f"k_gemm ({info['mfma']} scaled MFMA)",
                     "algorithmic": f"{info['flops']:.4g} FLOP per launch"}
         value = info["flops"] / (step_ms * 1e-3) / 1e12
@@ -252,7 +278,8 @@ def main():
         n = names[0]
         gbs = info["qbytes"][n] / (kernel_ms[n] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(args.workload),
                     "kernel": "k_quant dual layout"}
         value = gbs
         metric = "mx_quantize GB/s (% HBM peak)"
