@@ -12,17 +12,18 @@
 // C[M][N] = alpha' * A[M][K] . B[N][K]^T, A/B as written by the quantizer
 // (K contiguous codes, [rows][K/32] E8M0 scales).
 //
-// Tiling: 256x256 output tile per 256-thread workgroup (2x2 waves, 128x128
-// per wave = 4x4 MFMA 32x32 tiles, fp32 accumulators in AGPRs).  K advances
-// 128 bytes per row per stage (128 FP8 / 256 FP4 elements).  Stages are
-// double-buffered in LDS and filled by direct global->LDS loads
-// (global_load_lds_dwordx4: lane i of a wave writes bytes [16i, 16i+16) of a
-// 1 KiB run), so operand tiles never pass through VGPRs.  The 16-byte chunks
-// of each 128-byte LDS row are XOR-swizzled by (row >> 1) & 7 -- applied on the
-// global side by choosing which chunk each lane fetches -- which keeps the
-// ds_read_b128 operand fetches free of bank conflicts.  A ragged last K
-// stage (K not a multiple of the stage) is loaded through registers with
-// zero fill.
+// Tiling: 256x256 output tile per 512-thread workgroup (2x4 waves, 128x64
+// per wave = 4x2 MFMA 32x32 tiles, fp32 accumulators in AGPRs).  Two waves
+// share each SIMD, so one wave's fragment reads and stage waits overlap the
+// other's MFMAs.  K advances 128 bytes per row per stage (128 FP8 / 256 FP4
+// elements).  Stages are double-buffered in LDS and filled by direct
+// global->LDS loads (global_load_lds_dwordx4: lane i of a wave writes bytes
+// [16i, 16i+16) of a 1 KiB run), so operand tiles never pass through VGPRs.
+// The 16-byte chunks of each 128-byte LDS row are XOR-swizzled by
+// (row >> 1) & 7 -- applied on the global side by choosing which chunk each
+// lane fetches -- which keeps the ds_read_b128 operand fetches free of bank
+// conflicts.  A ragged last K stage (K not a multiple of the stage) is loaded
+// through registers with zero fill.
 //
 // Operand lane layout of the 32x32x64 scaled MFMA (lane l, h = l / 32, row
 // or column l % 32), established with on-device probes:
@@ -102,19 +103,19 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& t
 // Ties the accumulators to this point of the program: the MFMA builtins
 // have no side effects, so without it the compiler may sink a stage's MFMAs
 // past the end-of-stage wait and barrier, which serializes the loads.
-__device__ __forceinline__ void pin(f16v (&acc)[4][4])
+__device__ __forceinline__ void pin(f16v (&acc)[4][2])
 {
 #if defined(__HIP_DEVICE_COMPILE__)      // AGPR constraint: device pass only
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < 2; j++) asm volatile("" : "+a"(acc[i][j]));
 #endif
 }
 
-// One LDS stage of MFMAs for a wave's 128x128 sub-tile (4x4 tiles of 32x32).
+// One LDS stage of MFMAs for a wave's 128x64 sub-tile (4x2 tiles of 32x32).
 template <int FA, int FB>
-__device__ __forceinline__ void mma_stage(f16v (&acc)[4][4], const uint8_t* sA, const uint8_t* sB,
+__device__ __forceinline__ void mma_stage(f16v (&acc)[4][2], const uint8_t* sA, const uint8_t* sB,
                                           const uint32_t* sSA, const uint32_t* sSB, int wm, int wn,
                                           int h, int l32)
 {
@@ -124,39 +125,45 @@ __device__ __forceinline__ void mma_stage(f16v (&acc)[4][4], const uint8_t* sA, 
     constexpr int KSTEPS = BKB * EPB / 64;           // MFMA k-steps per stage (2 or 4)
     // scale registers: the lane's row, shifted so block (2*ks + h) sits at
     // byte 2*(ks%2) of dword ks/2
-    uint32_t sca[4][SB / 4], scb[4][SB / 4];
+    uint32_t sca[4][SB / 4], scb[2][SB / 4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int w = 0; w < SB / 4; w++) {
 #pragma unroll
-        for (int w = 0; w < SB / 4; w++) {
-            sca[i][w] = sSA[w * BM + wm * 128 + i * 32 + l32] >> (8 * h);
-            scb[i][w] = sSB[w * BM + wn * 128 + i * 32 + l32] >> (8 * h);
-        }
+        for (int i = 0; i < 4; i++) sca[i][w] = sSA[w * BM + wm * 128 + i * 32 + l32] >> (8 * h);
+#pragma unroll
+        for (int j = 0; j < 2; j++) scb[j][w] = sSB[w * BM + wn * 64 + j * 32 + l32] >> (8 * h);
+    }
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ks++) {
-        int8v fa[4], fb[4];
+        int8v fa[4], fb[2];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int ra_row = wm * 128 + i * 32 + l32;
-            const int rb_row = wn * 128 + i * 32 + l32;
             if constexpr (!FP4) {
                 const uint4 a0 = *(const uint4*)(sA + swz(ra_row, ks * 4 + h));
                 const uint4 a1 = *(const uint4*)(sA + swz(ra_row, ks * 4 + 2 + h));
-                const uint4 b0 = *(const uint4*)(sB + swz(rb_row, ks * 4 + h));
-                const uint4 b1 = *(const uint4*)(sB + swz(rb_row, ks * 4 + 2 + h));
                 fa[i] = int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                fb[i] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
             } else {
                 const uint4 a0 = *(const uint4*)(sA + swz(ra_row, ks * 2 + h));
-                const uint4 b0 = *(const uint4*)(sB + swz(rb_row, ks * 2 + h));
                 fa[i] = int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
-                fb[i] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int rb_row = wn * 64 + j * 32 + l32;
+            if constexpr (!FP4) {
+                const uint4 b0 = *(const uint4*)(sB + swz(rb_row, ks * 4 + h));
+                const uint4 b1 = *(const uint4*)(sB + swz(rb_row, ks * 4 + 2 + h));
+                fb[j] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            } else {
+                const uint4 b0 = *(const uint4*)(sB + swz(rb_row, ks * 2 + h));
+                fb[j] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
             }
         }
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
+            for (int j = 0; j < 2; j++) {
                 const int w = ks / 2;                     // scale dword
                 if ((ks & 1) == 0)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -171,7 +178,7 @@ __device__ __forceinline__ void mma_stage(f16v (&acc)[4][4], const uint8_t* sA, 
 }
 
 template <int FA, int FB, int OUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm(GArgs g)
 {
 #if defined(__HIP_DEVICE_COMPILE__)      // the host pass only needs the launch stub
@@ -189,7 +196,7 @@ void k_gemm(GArgs g)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int h = lane >> 5, l32 = lane & 31;
 
     int tm, tn;
@@ -203,14 +210,14 @@ void k_gemm(GArgs g)
 
     // ---- stage loads ----
     // direct: bounds-checked buffer loads straight into LDS.  Wave w, load p
-    // covers tile rows 32p + 8w .. +8; lane -> row (lane / 8) of that run and
-    // LDS slot (lane % 8), which receives global chunk slot ^ (row & 7).  The
-    // buffer of load p starts at tile row 32p of the stage and ends at row M
-    // (N), so rows past the matrix read as zero.  Only the lane's 32-bit
-    // offset lives in a VGPR.
-    const int lrow = 8 * wave + (lane >> 3);                  // row within a 32-row run
+    // covers tile rows 64p + 8w .. +8; lane -> row (lane / 8) of that run and
+    // LDS slot (lane % 8), which receives global chunk slot ^ key(row).  The
+    // buffer of a stage starts at tile row 0 and ends at row M (N), so rows
+    // past the matrix read as zero.  Only the lane's 32-bit offset lives in a
+    // VGPR.  Scales: waves 0-3 load A's, waves 4-7 B's, 64 rows each.
+    const int lrow = 8 * wave + (lane >> 3);                  // row within a 64-row run
     const uint32_t voff = (uint32_t)(lrow * kbytes + (((lane & 7) ^ swz_key(lrow)) << 4));
-    const uint32_t soff_row = (uint32_t)((64 * wave + lane) * kblocks);
+    const uint32_t soff_row = (uint32_t)((64 * (wave & 3) + lane) * kblocks);
     auto rsrc = [&](const uint8_t* base, int64_t first_row, int64_t rows, int64_t row_bytes,
                     int64_t col0) {
         int64_t n = (rows - first_row) * row_bytes - col0;
@@ -223,31 +230,33 @@ void k_gemm(GArgs g)
         const auto ra = rsrc(g.qa, m0, g.M, kbytes, kb0);
         const auto rb = rsrc(g.qb, n0, g.N, kbytes, kb0);
 #pragma unroll
-        for (int p = 0; p < 8; p++) {
-            const uint32_t off = voff + (uint32_t)(32 * p * kbytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + (32 * p + 8 * wave) * BKB), 16,
+        for (int p = 0; p < 4; p++) {
+            const uint32_t off = voff + (uint32_t)(64 * p * kbytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + (64 * p + 8 * wave) * BKB), 16,
                                                      off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sB + (32 * p + 8 * wave) * BKB), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sB + (64 * p + 8 * wave) * BKB), 16,
                                                      off, 0, 0, 0);
         }
         // scales: plane w holds bytes [4w, 4w+4) of every row's stage scales
 #pragma unroll
         for (int w = 0; w < SB / 4; w++) {
             const int64_t blk = (int64_t)s * SB + 4 * w;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(g.sa, m0, g.M, kblocks, blk),
-                                                     (lds_void*)(sSA + w * BM + 64 * wave), 4,
-                                                     soff_row, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(g.sb, n0, g.N, kblocks, blk),
-                                                     (lds_void*)(sSB + w * BM + 64 * wave), 4,
-                                                     soff_row, 0, 0, 0);
+            if (wave < 4)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(g.sa, m0, g.M, kblocks, blk),
+                                                         (lds_void*)(sSA + w * BM + 64 * wave), 4,
+                                                         soff_row, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(g.sb, n0, g.N, kblocks, blk),
+                                                         (lds_void*)(sSB + w * BM + 64 * (wave - 4)), 4,
+                                                         soff_row, 0, 0, 0);
         }
     };
     // register path with zero fill for a ragged last stage
     auto load_tail = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) {
         const int64_t kb0 = (int64_t)s * BKB;
 #pragma unroll
-        for (int p = 0; p < 8; p++) {
-            const int id = p * 256 + tid;
+        for (int p = 0; p < 4; p++) {
+            const int id = p * 512 + tid;
             const int row = id >> 3, chunk = id & 7;
             const int64_t kb = kb0 + chunk * 16;
             const int64_t ar = min(m0 + row, g.M - 1), br = min(n0 + row, g.N - 1);
@@ -259,20 +268,20 @@ void k_gemm(GArgs g)
             *(uint4*)(sA + swz(row, chunk)) = va;
             *(uint4*)(sB + swz(row, chunk)) = vb;
         }
-        const int64_t ar = min(m0 + tid, g.M - 1), br = min(n0 + tid, g.N - 1);
+        // scales: threads 0-255 A's rows, 256-511 B's
+        const bool opb = tid >= 256;
+        const int r = tid & 255;
+        const uint8_t* sc = opb ? g.sb : g.sa;
+        const int64_t rr = opb ? min(n0 + r, g.N - 1) : min(m0 + r, g.M - 1);
 #pragma unroll
         for (int w = 0; w < SB / 4; w++) {
-            uint32_t va = 0, vb = 0;
+            uint32_t v = 0;
 #pragma unroll
             for (int b = 0; b < 4; b++) {
                 const int64_t blk = (int64_t)s * SB + 4 * w + b;
-                const uint32_t xa = blk < kblocks ? g.sa[ar * kblocks + blk] : 127u;
-                const uint32_t xb = blk < kblocks ? g.sb[br * kblocks + blk] : 127u;
-                va |= xa << (8 * b);
-                vb |= xb << (8 * b);
+                v |= (blk < kblocks ? (uint32_t)sc[rr * kblocks + blk] : 127u) << (8 * b);
             }
-            sSA[w * BM + tid] = va;
-            sSB[w * BM + tid] = vb;
+            (opb ? sSB : sSA)[w * BM + r] = v;
         }
     };
     auto load_stage = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) {
@@ -280,11 +289,11 @@ void k_gemm(GArgs g)
         else load_direct(s, sA, sB, sSA, sSB);
     };
 
-    f16v acc[4][4];
+    f16v acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
@@ -317,31 +326,31 @@ void k_gemm(GArgs g)
     if (g.hadamard_k) ap = ap * 0.03125f;
 
     if constexpr (OUT == 1) {
-        // bf16: each wave stages its 128x128 sub-tile (256-byte rows) in its
-        // own 32 KiB of LDS, then writes 16-byte runs of 8 columns
-        uint8_t* region = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
-        uint16_t* ct = (uint16_t*)region;
+        // bf16: each wave stages its 128x64 sub-tile (128-byte rows) in its
+        // own 16 KiB of LDS, then writes 16-byte runs of 8 columns
+        uint8_t* buf = (wave >> 1) == 0 ? lA0 : (wave >> 1) == 1 ? lA1 : (wave >> 1) == 2 ? lB0 : lB1;
+        uint16_t* ct = (uint16_t*)(buf + (wave & 1) * 16384);
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < 2; j++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int row = i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                     const int col = j * 32 + l32;
-                    ct[row * 128 + col] = f32_to_bf16_rne(acc[i][j][r] * ap);
+                    ct[row * 64 + col] = f32_to_bf16_rne(acc[i][j][r] * ap);
                 }
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
         const bool vec = (g.ldc % 8) == 0 && (((uintptr_t)g.c) & 15u) == 0;
-        const int64_t rbase = m0 + wm * 128, cbase = n0 + wn * 128;
+        const int64_t rbase = m0 + wm * 128, cbase = n0 + wn * 64;
 #pragma unroll 4
-        for (int p = 0; p < 32; p++) {
+        for (int p = 0; p < 16; p++) {
             const int id = p * 64 + lane;
-            const int row = id >> 4, c8 = (id & 15) * 8;
+            const int row = id >> 3, c8 = (id & 7) * 8;
             const int64_t grow = rbase + row, gcol = cbase + c8;
             if (grow >= g.M) continue;
-            const uint4 v = *(const uint4*)(ct + row * 128 + c8);
+            const uint4 v = *(const uint4*)(ct + row * 64 + c8);
             uint16_t* dst = (uint16_t*)g.c + grow * g.ldc + gcol;
             if (vec && gcol + 8 <= g.N) {
                 *(uint4*)dst = v;
@@ -355,8 +364,8 @@ void k_gemm(GArgs g)
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int64_t col = n0 + wn * 128 + j * 32 + l32;
+            for (int j = 0; j < 2; j++) {
+                const int64_t col = n0 + wn * 64 + j * 32 + l32;
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
@@ -371,7 +380,7 @@ template <int FA, int FB, int OUT>
 hipError_t launch3(const GArgs& a, hipStream_t s)
 {
     const unsigned nwg = (unsigned)(a.tiles_m * a.tiles_n);
-    k_gemm<FA, FB, OUT><<<dim3(nwg), dim3(256), 0, s>>>(a);
+    k_gemm<FA, FB, OUT><<<dim3(nwg), dim3(512), 0, s>>>(a);
     return hipGetLastError();
 }
 
