@@ -155,6 +155,65 @@ def setup_fp4(args):
     return step, info
 
 
+# the six training GEMMs of one Llama-3-8B MLP layer: (name, A tensor, A copy,
+# A format, B tensor, B copy, B format); C[M][N] = A[M][K] . B[N][K]^T with
+# both operands K-contiguous, as the dual-layout quantizer writes them
+LLAMA_GEMMS = [
+    ("fprop_gate_up", "X", "row", "e4m3", "W_gu", "col", "e4m3"),
+    ("fprop_down", "Xp", "row", "e4m3", "W_d", "col", "e4m3"),
+    ("dgrad_gate_up", "dY_gu", "row", "e5m2", "W_gu", "row", "e4m3"),
+    ("dgrad_down", "dY_d", "row", "e5m2", "W_d", "row", "e4m3"),
+    ("wgrad_gate_up", "X", "col", "e4m3", "dY_gu", "col", "e5m2"),
+    ("wgrad_down", "Xp", "col", "e4m3", "dY_d", "col", "e5m2"),
+]
+
+
+def setup_llama(args):
+    """Llama-3-8B-shaped MLP training step (tokens 8192, hidden 4096, ffn
+    14336): dual-layout quantization of the six operand tensors (E4M3 for
+    activations and weights, E5M2 for gradients), then the six GEMMs."""
+    w = I.make("llama3_8b_mlp")
+    fmts = {"X": "e4m3", "Xp": "e4m3", "W_gu": "e4m3", "W_d": "e4m3", "dY_gu": "e5m2", "dY_d": "e5m2"}
+    src, outs = {}, {}
+    for name, fmt in fmts.items():
+        x = to_dev(w.tensors[name])
+        R, Cc = x.shape
+        src[name] = x
+        outs[name] = (torch.empty((R, Cc), dtype=torch.uint8, device="cuda"),
+                      torch.empty((R, Cc // 32), dtype=torch.uint8, device="cuda"),
+                      torch.empty((Cc, R), dtype=torch.uint8, device="cuda"),
+                      torch.empty((Cc, R // 32), dtype=torch.uint8, device="cuda"))
+    w.tensors.clear()                         # host copies are not needed any more
+    gemms, flops = [], 0.0
+    for gname, an, aax, fa, bn, bax, fb in LLAMA_GEMMS:
+        A, B = src[an], src[bn]
+        M = A.shape[0] if aax == "row" else A.shape[1]
+        K = A.shape[1] if aax == "row" else A.shape[0]
+        N = B.shape[1] if bax == "col" else B.shape[0]
+        qa, sa = outs[an][:2] if aax == "row" else outs[an][2:]
+        qb, sb = outs[bn][:2] if bax == "row" else outs[bn][2:]
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        gemms.append((gname, qa, sa, fa, qb, sb, fb, M, N, K, C))
+        flops += 2.0 * M * N * K
+
+    def step(t):
+        for name, fmt in fmts.items():
+            t.run("quant_" + name, lambda name=name, fmt=fmt: mx.mx_quantize_dual_layout(
+                src[name], mx.qconfig(fmt), *outs[name]))
+        for gname, qa, sa, fa, qb, sb, fb, M, N, K, C in gemms:
+            t.run(gname, lambda qa=qa, sa=sa, fa=fa, qb=qb, sb=sb, fb=fb, M=M, N=N, K=K, C=C: mx.mx_gemm(
+                qa, sa, None, fa, qb, sb, None, fb, M, N, K, out_dtype=mx.MX_OUT_BF16, c=C))
+
+    # per element: 2 bytes read, a code byte in each copy, two scale bytes per 32
+    qbytes = {"quant_" + n: 4 * int(src[n].numel()) + 2 * (int(src[n].numel()) // 32) for n in fmts}
+    info = dict(flops=flops, qbytes=qbytes, gemm_kernel=[g[0] for g in gemms], mfma="fp8",
+                config={"workload": "llama3_8b_mlp_train", "tokens": 8192, "hidden": 4096, "ffn": 14336,
+                        "gemms": [g[0] for g in gemms], "elem": "e4m3 (x, w) / e5m2 (dy)",
+                        "quantizer": "dual layout, 1x32 + 32x1 e8m0", "out": "bf16"},
+                host={})
+    return step, info
+
+
 def setup_copy(args):
     """A plain 512 MiB device copy: the reference that scales the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) of a profiling run."""
@@ -171,7 +230,8 @@ def setup_copy(args):
     return step, info
 
 
-WORKLOADS = {"moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4, "copy": setup_copy}
+WORKLOADS = {"moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4, "llama": setup_llama,
+             "copy": setup_copy}
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -264,7 +324,8 @@ def main():
         quant[n] = {"ms": round(kernel_ms[n], 4), "GB/s": round(gbs, 1),
                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(b)}
     if info["gemm_kernel"]:
-        g_ms = kernel_ms[info["gemm_kernel"]]
+        gk = info["gemm_kernel"]
+        g_ms = sum(kernel_ms[n] for n in gk) if isinstance(gk, list) else kernel_ms[gk]
         g_tf = info["flops"] / (g_ms * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[info["mfma"]]
         roofline = {"bound": "mfma", "achieved": round(g_tf, 2), "peak": peak, "unit": "TFLOP/s",
@@ -295,8 +356,11 @@ def main():
                      f"{args.flush} (not timed)" if flush is not None else
                      "HIP events on the launch stream; no cache eviction between steps"}
     if info["gemm_kernel"]:
-        out["kernels"]["gemm"] = {"ms": round(kernel_ms[info["gemm_kernel"]], 4),
-                                  "TFLOP/s": roofline["achieved"], "frac_mfma": roofline["frac"]}
+        out["kernels"]["gemm"] = {"ms": round(g_ms, 4), "TFLOP/s": roofline["achieved"],
+                                  "frac_mfma": roofline["frac"]}
+        if isinstance(info["gemm_kernel"], list):
+            for n in info["gemm_kernel"]:
+                out["kernels"][n] = {"ms": round(kernel_ms[n], 4)}
     if args.workload == "moss" and not args.no_cpu_baseline:
         log("timing the oracle on the host (bounded sample)")
         out["cpu_baseline"] = cpu_baseline_moss(info["host"])
