@@ -14,11 +14,18 @@
 //
 // Tiling: 256x256 output tile per 512-thread workgroup (2x4 waves, 128x64
 // per wave = 4x2 MFMA 32x32 tiles, fp32 accumulators in AGPRs).  Two waves
-// share each SIMD, so one wave's fragment reads and stage waits overlap the
-// other's MFMAs.  K advances 128 bytes per row per stage (128 FP8 / 256 FP4
-// elements).  Stages are double-buffered in LDS and filled by direct
-// global->LDS loads (global_load_lds_dwordx4: lane i of a wave writes bytes
-// [16i, 16i+16) of a 1 KiB run), so operand tiles never pass through VGPRs.
+// share each SIMD.  They run a two-group schedule: waves 0-3 and 4-7
+// alternate phases one MFMA k-step long, one group issuing the MFMAs of a
+// k-step from registers while the other reads its next operands from LDS,
+// with a fence-free workgroup barrier between phases.  K advances 128 bytes
+// per row per stage (128 FP8 / 256 FP4 elements).  Stages are double-buffered
+// in LDS and filled by direct global->LDS loads (buffer_load_dwordx4 ... lds:
+// lane i of a wave writes bytes [16i, 16i+16) of a 1 KiB run), so operand
+// tiles never pass through VGPRs.  Waves 0-3 issue those loads, spread over
+// their first read phase and first MFMA phase of a stage.  The per-CU rate
+// of these loads (about 64 GB/s measured) is as much of a limit as the MFMA
+// rate at this tile size: one stage's 64 KiB take about as long to arrive
+// as the stage's MFMAs take to run.
 // The 16-byte chunks of each 128-byte LDS row are XOR-swizzled by
 // (row >> 1) & 7 -- applied on the global side by choosing which chunk each
 // lane fetches -- which keeps the ds_read_b128 operand fetches free of bank
@@ -101,8 +108,8 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& t
 }
 
 // Ties the accumulators to this point of the program: the MFMA builtins
-// have no side effects, so without it the compiler may sink a stage's MFMAs
-// past the end-of-stage wait and barrier, which serializes the loads.
+// have no side effects, so without it the compiler may sink a phase's MFMAs
+// past the barrier that ends the phase.
 __device__ __forceinline__ void pin(f16v (&acc)[4][2])
 {
 #if defined(__HIP_DEVICE_COMPILE__)      // AGPR constraint: device pass only
@@ -113,68 +120,128 @@ __device__ __forceinline__ void pin(f16v (&acc)[4][2])
 #endif
 }
 
-// One LDS stage of MFMAs for a wave's 128x64 sub-tile (4x2 tiles of 32x32).
-template <int FA, int FB>
-__device__ __forceinline__ void mma_stage(f16v (&acc)[4][2], const uint8_t* sA, const uint8_t* sB,
-                                          const uint32_t* sSA, const uint32_t* sSB, int wm, int wn,
-                                          int h, int l32)
+// Operands of one MFMA k-step (64 elements of K) for a wave's 128x64
+// sub-tile, held in registers from the read phase to the MFMA phase of the
+// two-group schedule; scale dwords pre-shifted so the lane's block sits at
+// byte 2*(ks%2).
+// (FP4 operands fill only the low half of the MFMA's 8-dword source: the
+// instruction reads 4 registers for that format, so only those are held.)
+typedef int int4v __attribute__((ext_vector_type(4)));
+template <bool FP4>
+struct KFrag {
+    typedef typename std::conditional<FP4, int4v, int8v>::type V;
+    V a[4], b[2];
+    uint32_t sa[4], sb[2];
+};
+
+template <bool FP4>
+__device__ __forceinline__ int8v mfma_src(const typename KFrag<FP4>::V& v)
 {
-    constexpr bool FP4 = (FA == E2M1);
-    constexpr int EPB = FP4 ? 2 : 1;
-    constexpr int SB = BKB * EPB / 32;               // scale bytes per row per stage (4 or 8)
-    constexpr int KSTEPS = BKB * EPB / 64;           // MFMA k-steps per stage (2 or 4)
-    // scale registers: the lane's row, shifted so block (2*ks + h) sits at
-    // byte 2*(ks%2) of dword ks/2
-    uint32_t sca[4][SB / 4], scb[2][SB / 4];
+    if constexpr (FP4) return int8v{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+    else return v;
+}
+
+// Lane offsets into an operand tile, re-derived in every read phase: they
+// pass through an empty asm first, so the compiler recomputes the few
+// addresses of a phase from them instead of keeping every phase's addresses
+// live across the whole K loop.
+struct LaneOffs {
+    uint32_t a, b;        // byte offset of the lane's first A / B row (row * BKB)
+    uint32_t hk;          // (h ^ swizzle key of the lane's rows) << 4
+    uint32_t sa, sb;      // scale-plane index of the lane's first A / B row
+};
+
+template <bool FP4>
+__device__ __forceinline__ void read_kstep(KFrag<FP4>& f, const uint8_t* sA, const uint8_t* sB,
+                                           const uint32_t* sSA, const uint32_t* sSB, int ks, LaneOffs o,
+                                           int h)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(o.a), "+v"(o.b), "+v"(o.hk), "+v"(o.sa), "+v"(o.sb));
+#endif
+    // chunk (c ^ key) of the lane's rows, for c = cbase + h: rows 32 apart
+    // share the key, so one offset serves all row tiles of the operand
+    auto cofs = [&](int cbase) { return ((uint32_t)cbase << 4) ^ o.hk; };
+    auto frag = [&](const uint8_t* base, uint32_t lane_off, int t) {
+        if constexpr (!FP4) {
+            const uint4 c0 = *(const uint4*)(base + lane_off + cofs(ks * 4) + t * 32 * BKB);
+            const uint4 c1 = *(const uint4*)(base + lane_off + cofs(ks * 4 + 2) + t * 32 * BKB);
+            return int8v{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+        } else {
+            const uint4 c0 = *(const uint4*)(base + lane_off + cofs(ks * 2) + t * 32 * BKB);
+            return int4v{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w};
+        }
+    };
 #pragma unroll
-    for (int w = 0; w < SB / 4; w++) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) sca[i][w] = sSA[w * BM + wm * 128 + i * 32 + l32] >> (8 * h);
-#pragma unroll
-        for (int j = 0; j < 2; j++) scb[j][w] = sSB[w * BM + wn * 64 + j * 32 + l32] >> (8 * h);
+    for (int i = 0; i < 4; i++) {
+        f.a[i] = frag(sA, o.a, i);
+        f.sa[i] = sSA[(ks / 2) * BM + o.sa + i * 32] >> (8 * h);
     }
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ks++) {
-        int8v fa[4], fb[2];
+    for (int j = 0; j < 2; j++) {
+        f.b[j] = frag(sB, o.b, j);
+        f.sb[j] = sSB[(ks / 2) * BM + o.sb + j * 32] >> (8 * h);
+    }
+}
+
+// Makes the operands look redefined at this point of the program, so that
+// the MFMAs that use them cannot be hoisted above it (they have no memory
+// side effects, and the phase barriers only order memory).
+template <bool FP4>
+__device__ __forceinline__ void hold(KFrag<FP4>& f)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]), "+v"(f.b[1]));
+    asm volatile("" : "+v"(f.sa[0]), "+v"(f.sa[1]), "+v"(f.sa[2]), "+v"(f.sa[3]), "+v"(f.sb[0]), "+v"(f.sb[1]));
+#endif
+}
+
+// One k-step of MFMAs; after MFMA m (0..7) calls between(m), in program order.
+template <int FA, int FB, typename Between>
+__device__ __forceinline__ void mma_kstep_with(f16v (&acc)[4][2], const KFrag<FA == E2M1>& f, int ks, Between between)
+{
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int ra_row = wm * 128 + i * 32 + l32;
-            if constexpr (!FP4) {
-                const uint4 a0 = *(const uint4*)(sA + swz(ra_row, ks * 4 + h));
-                const uint4 a1 = *(const uint4*)(sA + swz(ra_row, ks * 4 + 2 + h));
-                fa[i] = int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-            } else {
-                const uint4 a0 = *(const uint4*)(sA + swz(ra_row, ks * 2 + h));
-                fa[i] = int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
-            }
-        }
+    for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const int rb_row = wn * 64 + j * 32 + l32;
-            if constexpr (!FP4) {
-                const uint4 b0 = *(const uint4*)(sB + swz(rb_row, ks * 4 + h));
-                const uint4 b1 = *(const uint4*)(sB + swz(rb_row, ks * 4 + 2 + h));
-                fb[j] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-            } else {
-                const uint4 b0 = *(const uint4*)(sB + swz(rb_row, ks * 2 + h));
-                fb[j] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
-            }
+            if ((ks & 1) == 0)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    mfma_src<FA == E2M1>(f.a[i]), mfma_src<FA == E2M1>(f.b[j]), acc[i][j], MfmaFmt<FA>::code, MfmaFmt<FB>::code, 0, (int)f.sa[i], 0,
+                    (int)f.sb[j]);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    mfma_src<FA == E2M1>(f.a[i]), mfma_src<FA == E2M1>(f.b[j]), acc[i][j], MfmaFmt<FA>::code, MfmaFmt<FB>::code, 2, (int)f.sa[i], 2,
+                    (int)f.sb[j]);
+            __builtin_amdgcn_sched_barrier(0);
+            between(2 * i + j);
+            __builtin_amdgcn_sched_barrier(0);
         }
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ void mma_kstep(f16v (&acc)[4][2], const KFrag<FA == E2M1>& f, int ks)
+{
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const int w = ks / 2;                     // scale dword
-                if ((ks & 1) == 0)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fa[i], fb[j], acc[i][j], MfmaFmt<FA>::code, MfmaFmt<FB>::code,
-                        0, (int)sca[i][w], 0, (int)scb[j][w]);
-                else
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fa[i], fb[j], acc[i][j], MfmaFmt<FA>::code, MfmaFmt<FB>::code,
-                        2, (int)sca[i][w], 2, (int)scb[j][w]);
-            }
-    }
+        for (int j = 0; j < 2; j++) {
+            if ((ks & 1) == 0)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    mfma_src<FA == E2M1>(f.a[i]), mfma_src<FA == E2M1>(f.b[j]), acc[i][j], MfmaFmt<FA>::code, MfmaFmt<FB>::code, 0, (int)f.sa[i], 0,
+                    (int)f.sb[j]);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    mfma_src<FA == E2M1>(f.a[i]), mfma_src<FA == E2M1>(f.b[j]), acc[i][j], MfmaFmt<FA>::code, MfmaFmt<FB>::code, 2, (int)f.sa[i], 2,
+                    (int)f.sb[j]);
+        }
+}
+
+// Workgroup barrier between the phases of the two-group schedule: this wave's LDS reads complete, no
+// vector-memory wait, and the memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void half_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int FA, int FB, int OUT>
@@ -195,7 +262,8 @@ void k_gemm(GArgs g)
     __shared__ __align__(16) uint32_t lSA0[2 * BM], lSA1[2 * BM], lSB0[2 * BM], lSB1[2 * BM];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
     const int wm = wave >> 2, wn = wave & 3;
     const int h = lane >> 5, l32 = lane & 31;
 
@@ -209,54 +277,61 @@ void k_gemm(GArgs g)
     const bool ragged = (kbytes % BKB) != 0;
 
     // ---- stage loads ----
+    // Loads are issued by waves 0-3 only.
     // direct: bounds-checked buffer loads straight into LDS.  Wave w, load p
-    // covers tile rows 64p + 8w .. +8; lane -> row (lane / 8) of that run and
+    // covers tile rows 32p + 8w .. +8; lane -> row (lane / 8) of that run and
     // LDS slot (lane % 8), which receives global chunk slot ^ key(row).  The
     // buffer of a stage starts at tile row 0 and ends at row M (N), so rows
     // past the matrix read as zero.  Only the lane's 32-bit offset lives in a
-    // VGPR.  Scales: waves 0-3 load A's, waves 4-7 B's, 64 rows each.
-    const int lrow = 8 * wave + (lane >> 3);                  // row within a 64-row run
+    // VGPR.  Scales: wave w loads rows 64w .. +64 of both operands.
+    const int lrow = 8 * (wave & 3) + (lane >> 3);            // row within a 32-row run
     const uint32_t voff = (uint32_t)(lrow * kbytes + (((lane & 7) ^ swz_key(lrow)) << 4));
     const uint32_t soff_row = (uint32_t)((64 * (wave & 3) + lane) * kblocks);
-    auto rsrc = [&](const uint8_t* base, int64_t first_row, int64_t rows, int64_t row_bytes,
-                    int64_t col0) {
-        int64_t n = (rows - first_row) * row_bytes - col0;
-        n = n < 0 ? 0 : (n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n);
-        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + first_row * row_bytes + col0),
-                                                 (short)0, (int)(uint32_t)n, 0x00020000);
+    // One descriptor per operand for the whole K loop, based at the tile's
+    // first row and ending at row M (N); the stage's K offset is added to the
+    // lane offset, so rows past the matrix still fall outside the range.
+    auto rsrc = [&](const uint8_t* base, int64_t first_row, int64_t rows, int64_t row_bytes) __attribute__((always_inline)) {
+        int64_t n = (rows - first_row) * row_bytes;
+        n = n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + first_row * row_bytes), (short)0,
+                                                 (int)(uint32_t)n, 0x00020000);
     };
-    auto load_direct = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) {
-        const int64_t kb0 = (int64_t)s * BKB;
-        const auto ra = rsrc(g.qa, m0, g.M, kbytes, kb0);
-        const auto rb = rsrc(g.qb, n0, g.N, kbytes, kb0);
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            const uint32_t off = voff + (uint32_t)(64 * p * kbytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + (64 * p + 8 * wave) * BKB), 16,
-                                                     off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sB + (64 * p + 8 * wave) * BKB), 16,
-                                                     off, 0, 0, 0);
-        }
-        // scales: plane w holds bytes [4w, 4w+4) of every row's stage scales
+    const auto ra = rsrc(g.qa, m0, g.M, kbytes), rb = rsrc(g.qb, n0, g.N, kbytes);
+    const auto rsa = rsrc(g.sa, m0, g.M, kblocks), rsb = rsrc(g.sb, n0, g.N, kblocks);
+    // Operand load instruction q (0..15) of stage s: run p = q / 2 of A (q
+    // even) or B (q odd); then the scale loads.
+    auto dma_op = [&](int s, int q, uint8_t* sA, uint8_t* sB) __attribute__((always_inline)) {
+        const int p = q >> 1;
+        uint32_t v = voff;
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" : "+v"(v));
+#endif
+        const uint32_t off = v + (uint32_t)(s * BKB) + (uint32_t)(32 * p * kbytes);
+        if (q & 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sB + (32 * p + 8 * wave) * BKB), 16, off, 0, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + (32 * p + 8 * wave) * BKB), 16, off, 0, 0, 0);
+    };
+    // scales: plane w holds bytes [4w, 4w+4) of every row's stage scales
+    auto dma_scales = [&](int s, uint32_t* sSA, uint32_t* sSB) __attribute__((always_inline)) {
 #pragma unroll
         for (int w = 0; w < SB / 4; w++) {
-            const int64_t blk = (int64_t)s * SB + 4 * w;
-            if (wave < 4)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(g.sa, m0, g.M, kblocks, blk),
-                                                         (lds_void*)(sSA + w * BM + 64 * wave), 4,
-                                                         soff_row, 0, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(g.sb, n0, g.N, kblocks, blk),
-                                                         (lds_void*)(sSB + w * BM + 64 * (wave - 4)), 4,
-                                                         soff_row, 0, 0, 0);
+            const uint32_t off = soff_row + (uint32_t)(s * SB + 4 * w);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(sSA + w * BM + 64 * wave), 4, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(sSB + w * BM + 64 * wave), 4, off, 0, 0, 0);
         }
     };
+    auto load_direct = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 16; q++) dma_op(s, q, sA, sB);
+        dma_scales(s, sSA, sSB);
+    };
     // register path with zero fill for a ragged last stage
-    auto load_tail = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) {
+    auto load_tail = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) __attribute__((always_inline)) {
         const int64_t kb0 = (int64_t)s * BKB;
 #pragma unroll
-        for (int p = 0; p < 4; p++) {
-            const int id = p * 512 + tid;
+        for (int p = 0; p < 8; p++) {
+            const int id = p * 256 + tid;
             const int row = id >> 3, chunk = id & 7;
             const int64_t kb = kb0 + chunk * 16;
             const int64_t ar = min(m0 + row, g.M - 1), br = min(n0 + row, g.N - 1);
@@ -268,23 +343,23 @@ void k_gemm(GArgs g)
             *(uint4*)(sA + swz(row, chunk)) = va;
             *(uint4*)(sB + swz(row, chunk)) = vb;
         }
-        // scales: threads 0-255 A's rows, 256-511 B's
-        const bool opb = tid >= 256;
-        const int r = tid & 255;
-        const uint8_t* sc = opb ? g.sb : g.sa;
-        const int64_t rr = opb ? min(n0 + r, g.N - 1) : min(m0 + r, g.M - 1);
+        const int64_t ar = min(m0 + tid, g.M - 1), br = min(n0 + tid, g.N - 1);
 #pragma unroll
         for (int w = 0; w < SB / 4; w++) {
-            uint32_t v = 0;
+            uint32_t va = 0, vb = 0;
 #pragma unroll
             for (int b = 0; b < 4; b++) {
                 const int64_t blk = (int64_t)s * SB + 4 * w + b;
-                v |= (blk < kblocks ? (uint32_t)sc[rr * kblocks + blk] : 127u) << (8 * b);
+                const uint32_t xa = blk < kblocks ? g.sa[ar * kblocks + blk] : 127u;
+                const uint32_t xb = blk < kblocks ? g.sb[br * kblocks + blk] : 127u;
+                va |= xa << (8 * b);
+                vb |= xb << (8 * b);
             }
-            (opb ? sSB : sSA)[w * BM + r] = v;
+            sSA[w * BM + tid] = va;
+            sSB[w * BM + tid] = vb;
         }
     };
-    auto load_stage = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) {
+    auto load_stage = [&](int s, uint8_t* sA, uint8_t* sB, uint32_t* sSA, uint32_t* sSB) __attribute__((always_inline)) {
         if (g.reg_path || (ragged && s == nstages - 1)) load_tail(s, sA, sB, sSA, sSB);
         else load_direct(s, sA, sB, sSA, sSB);
     };
@@ -297,27 +372,99 @@ void k_gemm(GArgs g)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-    load_stage(0, lA0, lB0, lSA0, lSB0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int s = 0;
-    for (; s + 1 < nstages; s += 2) {
-        // even stage in buffer 0 while stage s+1 streams into buffer 1
-        load_stage(s + 1, lA1, lB1, lSA1, lSB1);
-        mma_stage<FA, FB>(acc, lA0, lB0, lSA0, lSB0, wm, wn, h, l32);
-        pin(acc);                                  // keep this stage's MFMAs before the wait
-        __builtin_amdgcn_sched_barrier(0);
+    // Two-group schedule.  Waves 0-3 (group 0: rows 0-127 of the tile) and
+    // waves 4-7 (group 1: rows 128-255) share the SIMDs pairwise and
+    // alternate phases one MFMA k-step long: while one group runs the MFMAs
+    // of a k-step from registers, the other reads its operands of the next
+    // k-step from LDS, so each SIMD always holds a wave whose operands are
+    // ready.  With t counting k-steps over the whole K loop:
+    //   phase 2t-1: group 0 reads k-step t       | group 1 MFMAs of t-1
+    //   phase 2t  : group 0 MFMAs of k-step t    | group 1 reads t
+    // Group 0 also drives the loads: stage s+1 is issued in the phase where
+    // group 0 reads the first k-step of stage s -- its buffer was last read
+    // by group 1 in the phase before -- and awaited at the end of group 0's
+    // MFMAs of the last k-step of stage s.  Every phase ends with a workgroup
+    // barrier without a memory fence; both groups pass 2T+2 of them.
+    LaneOffs lo;
+    lo.a = (uint32_t)((wm * 128 + l32) * BKB);
+    lo.b = (uint32_t)((wn * 64 + l32) * BKB);
+    lo.hk = (uint32_t)((h ^ swz_key(l32)) << 4);
+    lo.sa = (uint32_t)(wm * 128 + l32);
+    lo.sb = (uint32_t)(wn * 64 + l32);
+    KFrag<FP4> f;
+    // FAST: every load is direct (no register path, no ragged stage); the
+    // other case keeps its loads out of the MFMA phases.
+    auto g0_stage = [&](auto fast, int s, const uint8_t* xA, const uint8_t* xB, const uint32_t* xSA,
+                        const uint32_t* xSB, uint8_t* yA, uint8_t* yB, uint32_t* ySA,
+                        uint32_t* ySB) __attribute__((always_inline)) {
+        constexpr bool FAST = decltype(fast)::value;
+        // In the fast case the next stage's loads are spread over the first
+        // read phase (scales and the first half) and the MFMAs of the first
+        // k-step (one instruction after each MFMA), so that no phase waits
+        // for the address unit to take all of them at once.
+        const bool next = s + 1 < nstages;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++) {
+            read_kstep<FP4>(f, xA, xB, xSA, xSB, ks, lo, h);
+            if (ks == 0 && next) {
+                if constexpr (FAST) {
+                    dma_scales(s + 1, ySA, ySB);
+#pragma unroll
+                    for (int q = 0; q < 8; q++) dma_op(s + 1, q, yA, yB);
+                } else {
+                    load_stage(s + 1, yA, yB, ySA, ySB);
+                }
+            }
+            half_barrier();
+            hold(f);
+            if (FAST && ks == 0 && next)
+                mma_kstep_with<FA, FB>(acc, f, ks, [&](int m) __attribute__((always_inline)) { dma_op(s + 1, 8 + m, yA, yB); });
+            else
+                mma_kstep<FA, FB>(acc, f, ks);
+            pin(acc);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks == KSTEPS - 1) __builtin_amdgcn_s_waitcnt(0);
+            half_barrier();
+        }
+    };
+    auto g0_run = [&](auto fast) __attribute__((always_inline)) {
+        if constexpr (decltype(fast)::value) load_direct(0, lA0, lB0, lSA0, lSB0);
+        else load_stage(0, lA0, lB0, lSA0, lSB0);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        // odd stage in buffer 1 while stage s+2 streams into buffer 0
-        if (s + 2 < nstages) load_stage(s + 2, lA0, lB0, lSA0, lSB0);
-        mma_stage<FA, FB>(acc, lA1, lB1, lSA1, lSB1, wm, wn, h, l32);
-        pin(acc);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        half_barrier();                                        // stage 0 landed
+        int s = 0;
+        for (; s + 1 < nstages; s += 2) {
+            g0_stage(fast, s, lA0, lB0, lSA0, lSB0, lA1, lB1, lSA1, lSB1);
+            g0_stage(fast, s + 1, lA1, lB1, lSA1, lSB1, lA0, lB0, lSA0, lSB0);
+        }
+        if (s < nstages) g0_stage(fast, s, lA0, lB0, lSA0, lSB0, lA1, lB1, lSA1, lSB1);
+        half_barrier();                                        // group 1's last MFMAs
+    };
+    auto g1_stage = [&](const uint8_t* xA, const uint8_t* xB, const uint32_t* xSA, const uint32_t* xSB) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ks++) {
+            read_kstep<FP4>(f, xA, xB, xSA, xSB, ks, lo, h);
+            half_barrier();
+            hold(f);
+            mma_kstep<FA, FB>(acc, f, ks);
+            pin(acc);
+            __builtin_amdgcn_sched_barrier(0);
+            half_barrier();
+        }
+    };
+    if (wave < 4) {
+        if (g.reg_path || ragged) g0_run(std::false_type{});
+        else g0_run(std::true_type{});
+    } else {
+        half_barrier();                                        // stage 0 landed
+        half_barrier();                                        // group 0 reads k-step 0
+        int s = 0;
+        for (; s + 1 < nstages; s += 2) {
+            g1_stage(lA0, lB0, lSA0, lSB0);
+            g1_stage(lA1, lB1, lSA1, lSB1);
+        }
+        if (s < nstages) g1_stage(lA0, lB0, lSA0, lSB0);
     }
-    if (s < nstages) mma_stage<FA, FB>(acc, lA0, lB0, lSA0, lSB0, wm, wn, h, l32);   // odd count
 
     // ---- epilogue: per-tensor scales once ----
     float ap = g.alpha;
