@@ -436,10 +436,10 @@ __device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt vmcnt(0)
 // 128 rows x 256 source bytes (128 bf16 or 64 fp32 columns).  NCW compute
 // waves plus one loader wave: the loader streams the next tile straight into
 // the other LDS buffer (direct global->LDS buffer loads, one 256-byte tile row
-// per instruction; rows past the tensor read as zero, columns past it hold
-// neighbouring data, and neither is used) while the compute waves quantize
-// the current one, so the compute waves never wait on a global load and the
-// loader never waits on a store.  Codes are staged back into the tile's own
+// per instruction; rows past the tensor are skipped, columns past it hold
+// neighbouring data or zeros, and neither is used) while the compute waves
+// quantize the current one, so the compute waves never wait on a global load
+// and the loader never waits on a store.  Codes are staged back into the tile's own
 // LDS buffer once every block has been read, then written out as whole runs:
 // each column's codes for the tile form one 128-byte (FP8) or 64-byte (FP4)
 // run of the transposed copy, each row's one run of the row copy, and scale
@@ -507,10 +507,22 @@ __global__ __launch_bounds__(64 * (DmaTile<SRC>::NCW + 1)) void k_quant_tile_dma
             const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)((const uint8_t*)a.x + (r0 * a.ld + c0) * EB), (short)0, (int)(uint32_t)n, 0x00020000);
             const uint32_t row_bytes = (uint32_t)(a.ld * EB);
+            // The buffer range check covers the lane offset, not soffset.  A
+            // tile whose 128 rows lie inside the tensor, and whose last row's
+            // 256 bytes do not run past the tensor's end, keeps the row
+            // offset in soffset; an edge tile loads only its rows inside the
+            // tensor, with the row offset in the checked lane offset.
+            if (a.rows - r0 >= TRR && (a.rows - r0 > TRR || a.cols - c0 >= TCC)) {
 #pragma unroll 8
-            for (int j = 0; j < TRR; j++)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + j * T::PITCH), 4, voff,
-                                                         j * row_bytes, 0, 0);
+                for (int j = 0; j < TRR; j++)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + j * T::PITCH), 4, voff,
+                                                             j * row_bytes, 0, 0);
+            } else {
+                const int nv = (int)(a.rows - r0 < TRR ? a.rows - r0 : TRR);
+                for (int j = 0; j < nv; j++)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + j * T::PITCH), 4,
+                                                             voff + j * row_bytes, 0, 0, 0);
+            }
         };
         int64_t r0, c0;
         if (tile_at<TRR, TCC>(a, 0, r0, c0)) issue(r0, c0, buf0);
