@@ -523,10 +523,334 @@ void k_gemm(GArgs g)
 #endif
 }
 
+// ---------------------------------------------------------------------------
+// k_gemm_w4: FP8 x FP8 with K a multiple of 128 and 4-byte aligned scale
+// arrays.  One wave per SIMD: a 256-thread workgroup computes the same
+// 256x256 tile, each wave a 128x128 quarter (4x4 MFMA 32x32 tiles, all 256
+// accumulator registers).  Compared with two 128x64 waves per SIMD this
+// reads a third less from LDS per MFMA (8 fragments per 16 MFMAs instead of
+// 6 per 8), and lets each wave overlap its own loads with its MFMAs instead
+// of trading phases with a partner wave at barriers.
+//
+// Operand tiles travel global -> registers -> LDS: each thread holds one
+// stage's share (16 chunks of 16 bytes, 64 VGPRs) between its global load
+// and its LDS write, which gives every load a whole stage to arrive.  Per
+// stage (128 bytes of K per row, two MFMA k-steps) each wave runs:
+//   phase A: the 16 MFMAs of k-step 0, each followed by one slot of other
+//            work: the LDS reads of k-step 1's fragments, and the LDS write
+//            and reload of part of a later stage;
+//   barrier (this wave's LDS reads and writes complete);
+//   phase B: the 16 MFMAs of k-step 1, each followed by the LDS reads of the
+//            next stage's k-step 0 fragments and the rest of the writes.
+// LDS holds two stage buffers (2 x 64 KiB plus scales); the schedule of the
+// writes into them is given at the main loop.  Rows past M (N) read as zero
+// and their outputs are dropped; loads of stages past the end re-read the
+// last stage into buffers nothing reads any more.
+//
+// Measured bound: with the loads taken out of the loop the same schedule
+// runs the MFMAs at 77% of the FP8 peak at long K, so the loads set the
+// pace.  Counters show each CU's vector-memory path saturated (address
+// unit busy >90%, L1 waiting on pending L2 data half the time) at about 19
+// bytes per clock against the 32 a 256x256 FP8 tile needs at the MFMA
+// rate, with an average L2 latency near 370 cycles.
+// k_gemm_w4's accumulators pinned to AGPRs (see pin above)
+__device__ __forceinline__ void pin4(f16v (&acc)[4][4])
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) asm volatile("" : "+a"(acc[i][j]));
+#endif
+}
+
+struct W4Frag {
+    int8v a[4], b[4];
+    uint32_t sa[4], sb[4];
+};
+
+template <int FA, int FB, int OUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_w4(GArgs g)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ __align__(16) uint8_t lA0[TILE_BYTES], lA1[TILE_BYTES];
+    __shared__ __align__(16) uint8_t lB0[TILE_BYTES], lB1[TILE_BYTES];
+    // scale dwords of a stage, [A rows | B rows], in two planes: plane 1 holds
+    // each dword shifted right by one byte, so a lane with h = 1 finds its
+    // blocks at bytes 0 and 2 without a shift after the read
+    __shared__ __align__(16) uint32_t lS0[4 * BM], lS1[4 * BM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    int tm, tn;
+    tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t kbytes = g.K;
+    const int64_t kblocks = g.K / 32;
+    const int nstages = (int)(kbytes / BKB);
+
+    // global loads of a stage: thread t moves 16-byte chunk (t & 7) of tile
+    // rows 32p + t/8 (p = 0..7) of A and of B, and the stage's scale dword
+    // of row t of A and of B.  Buffer loads: the row part of the offset is in
+    // the range-checked lane offset, so rows past M (N) read as zero; the
+    // stage's K offset rides in the unchecked scalar offset.
+    auto rsrc = [&](const uint8_t* base, int64_t first_row, int64_t rows, int64_t row_bytes) __attribute__((always_inline)) {
+        int64_t n = (rows - first_row) * row_bytes;
+        n = n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + first_row * row_bytes), (short)0,
+                                                 (int)(uint32_t)n, 0x00020000);
+    };
+    const auto ra = rsrc(g.qa, m0, g.M, kbytes), rb = rsrc(g.qb, n0, g.N, kbytes);
+    const auto rsa_ = rsrc(g.sa, m0, g.M, kblocks), rsb_ = rsrc(g.sb, n0, g.N, kblocks);
+    const int lr = tid >> 3, lc = tid & 7;
+    const uint32_t voff = (uint32_t)(lr * kbytes + lc * 16);
+    const uint32_t vsoff = (uint32_t)(tid * kblocks);
+    const uint32_t prow = (uint32_t)(32 * kbytes);        // offset of run p: p * prow
+    // LDS byte offset of the thread's chunk in run p: p * 32 * BKB + wofs
+    const uint32_t wofs = (uint32_t)swz(lr, lc);
+
+    uint4 stA[8], stB[8];
+    uint32_t stSA, stSB;
+    // L2 warm-up: four stages ahead of its loads, each workgroup touches a
+    // share of its A and B rows chosen so that the tiles sharing a panel on
+    // one XCD (a block of 4 tile rows x 8 tile columns) touch different
+    // rows -- 32 A rows by tile column, 64 B rows by tile row -- so most of
+    // the panel is in L2 by the time its owners load it.  The loads go
+    // straight to a scratch area of LDS that nothing reads (no registers).
+    // Measured: the per-CU load path is bound by L2 latency, and misses to
+    // the fabric are what raise it.
+    __shared__ __align__(16) uint8_t lPF[4 * 1024];
+    const uint32_t pfa = (uint32_t)((32 * (tn & 7) + 8 * wave + (lane >> 3)) * kbytes + (lane & 7) * 16);
+    const uint32_t pfb = (uint32_t)((64 * (tm & 3) + 16 * wave + (lane >> 3)) * kbytes + (lane & 7) * 16);
+    auto prefetch = [&](int s) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(lPF + wave * 1024), 16, pfa, s * BKB, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lPF + wave * 1024), 16, pfb, s * BKB, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lPF + wave * 1024), 16, pfb + 8 * (uint32_t)kbytes, s * BKB, 0, 0);
+    };
+    auto gl16 = [&](__amdgpu_buffer_rsrc_t r, int p, int s) __attribute__((always_inline)) {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + p * prow, s * BKB, 0));
+    };
+    auto gload = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            stA[p] = gl16(ra, p, s);
+            stB[p] = gl16(rb, p, s);
+        }
+        stSA = __builtin_amdgcn_raw_buffer_load_b32(rsa_, vsoff, s * 4, 0);
+        stSB = __builtin_amdgcn_raw_buffer_load_b32(rsb_, vsoff, s * 4, 0);
+    };
+
+    // fragment reads (same lane layout and swizzle as k_gemm)
+    const uint32_t oa = (uint32_t)((wm * 128 + l32) * BKB);
+    const uint32_t ob = (uint32_t)((wn * 128 + l32) * BKB);
+    const uint32_t hk = (uint32_t)((h ^ swz_key(l32)) << 4);
+    const int rsa = 2 * BM * h + wm * 128 + l32, rsb = 2 * BM * h + BM + wn * 128 + l32;
+    // fragment t (0..3: A tile t, 4..7: B tile t-4) of k-step ks
+    auto rd_frag = [&](W4Frag& f, const uint8_t* sA, const uint8_t* sB, int ks, int t) __attribute__((always_inline)) {
+        const uint32_t c0 = ((uint32_t)(ks * 4) << 4) ^ hk, c1 = ((uint32_t)(ks * 4 + 2) << 4) ^ hk;
+        const uint8_t* base = t < 4 ? sA + oa + (t & 3) * 32 * BKB : sB + ob + (t & 3) * 32 * BKB;
+        const uint4 v0 = *(const uint4*)(base + c0);
+        const uint4 v1 = *(const uint4*)(base + c1);
+        const int8v v = int8v{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        if (t < 4) f.a[t] = v;
+        else f.b[t - 4] = v;
+    };
+    // scale dword of tile t (t < 4: A, else B) with the lane's block of
+    // k-step ks at byte 2 * ks
+    auto rd_scale = [&](W4Frag& f, const uint32_t* sS, int t) __attribute__((always_inline)) {
+        if (t < 4) f.sa[t] = sS[rsa + 32 * t];
+        else f.sb[t - 4] = sS[rsb + 32 * (t - 4)];
+    };
+    auto wr_scales = [&](uint32_t* sS) __attribute__((always_inline)) {
+        sS[tid] = stSA;
+        sS[BM + tid] = stSB;
+        sS[2 * BM + tid] = stSA >> 8;
+        sS[3 * BM + tid] = stSB >> 8;
+    };
+    auto swrite_a = [&](uint8_t* sA, int p) __attribute__((always_inline)) { *(uint4*)(sA + p * 32 * BKB + wofs) = stA[p]; };
+    auto swrite_b = [&](uint8_t* sB, int p) __attribute__((always_inline)) { *(uint4*)(sB + p * 32 * BKB + wofs) = stB[p]; };
+
+    f16v acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    auto mma = [&](const W4Frag& f, int ks, int m) __attribute__((always_inline)) {
+        const int i = m >> 2, j = m & 3;
+        if (ks == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], MfmaFmt<FA>::code,
+                                                                        MfmaFmt<FB>::code, 0, (int)f.sa[i], 0, (int)f.sb[j]);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], MfmaFmt<FA>::code,
+                                                                        MfmaFmt<FB>::code, 2, (int)f.sa[i], 2, (int)f.sb[j]);
+    };
+
+    pin4(acc);
+    W4Frag F0, F1;
+    // prologue: stage 0 into buffer 0 and stage 1's A tile into buffer 1;
+    // stage 1's B tile and scales, and stage 2's A tile, left in flight
+    // (stage 1 is loaded into temporaries before stage 0 is waited for, so
+    // the two round trips overlap; the fragment registers are not live yet)
+    {
+        const int s1 = min(1, nstages - 1);
+        gload(0);
+        uint4 uA[8], uB[8];
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            uA[p] = gl16(ra, p, s1);
+            uB[p] = gl16(rb, p, s1);
+        }
+        const uint32_t uSA = __builtin_amdgcn_raw_buffer_load_b32(rsa_, vsoff, s1 * 4, 0);
+        const uint32_t uSB = __builtin_amdgcn_raw_buffer_load_b32(rsb_, vsoff, s1 * 4, 0);
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            swrite_a(lA0, p);
+            swrite_b(lB0, p);
+        }
+        wr_scales(lS0);
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            stA[p] = gl16(ra, p, min(2, nstages - 1));
+            *(uint4*)(lA1 + p * 32 * BKB + wofs) = uA[p];
+            stB[p] = uB[p];
+        }
+        stSA = uSA;
+        stSB = uSB;
+    }
+    half_barrier();
+#pragma unroll
+    for (int q = 0; q < 8; q++) rd_frag(F0, lA0, lB0, 0, q);
+#pragma unroll
+    for (int t = 0; t < 8; t++) rd_scale(F0, lS0, t);
+
+    // Stage s computes from buffer X and fills buffer Y with stage s+1 and
+    // X with stage s+2.  The LDS writes are split between the phases so
+    // that neither carries all of them: phase A writes stage s+1's B tile
+    // and scales to Y (the A tile went there in phase B of stage s-1) and
+    // reloads them with stage s+2; phase B, after the barrier that ends
+    // every read of X, writes stage s+2's A tile to X and reloads it with
+    // stage s+3.  Each register-held tile thus has a whole stage to arrive.
+    auto stage = [&](int s, uint8_t* xA, uint8_t* xB, uint32_t* xS, uint8_t* yA, uint8_t* yB,
+                     uint32_t* yS) __attribute__((always_inline)) {
+        const int s2 = min(s + 2, nstages - 1), s3 = min(s + 3, nstages - 1);
+        // phase A
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            mma(F0, 0, m);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < 8) {
+                rd_frag(F1, xA, xB, 1, m);
+                swrite_b(yB, m);
+                stB[m] = gl16(rb, m, s2);
+            } else {
+                rd_scale(F1, xS, m - 8);
+                if (m == 9) prefetch(min(s + 4, nstages - 1));
+                if (m == 8) {
+                    wr_scales(yS);
+                    stSA = __builtin_amdgcn_raw_buffer_load_b32(rsa_, vsoff, s2 * 4, 0);
+                    stSB = __builtin_amdgcn_raw_buffer_load_b32(rsb_, vsoff, s2 * 4, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pin4(acc);
+        half_barrier();
+        // phase B
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            mma(F1, 1, m);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < 8) {
+                rd_frag(F0, yA, yB, 0, m);
+            } else {
+                rd_scale(F0, yS, m - 8);
+                swrite_a(xA, m - 8);
+                stA[m - 8] = gl16(ra, m - 8, s3);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pin4(acc);
+    };
+    for (int s = 0; s < nstages; s += 2) {
+        stage(s, lA0, lB0, lS0, lA1, lB1, lS1);
+        if (s + 1 < nstages) stage(s + 1, lA1, lB1, lS1, lA0, lB0, lS0);
+    }
+
+    // ---- epilogue: per-tensor scales once ----
+    float ap = g.alpha;
+    if (g.ta) ap = ap * *g.ta;
+    if (g.tb) ap = ap * *g.tb;
+    if (g.hadamard_k) ap = ap * 0.03125f;
+    half_barrier();                                  // every wave done with the stage buffers
+
+    if constexpr (OUT == 1) {
+        // each wave stages its 128x128 quarter (256-byte rows) in 32 KiB of LDS
+        uint8_t* buf = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
+        uint16_t* ct = (uint16_t*)buf;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int row = i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                    const int col = j * 32 + l32;
+                    ct[row * 128 + col] = f32_to_bf16_rne(acc[i][j][r] * ap);
+                }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        const bool vec = (g.ldc % 8) == 0 && (((uintptr_t)g.c) & 15u) == 0;
+        const int64_t rbase = m0 + wm * 128, cbase = n0 + wn * 128;
+#pragma unroll 4
+        for (int p = 0; p < 32; p++) {
+            const int id = p * 64 + lane;
+            const int row = id >> 4, c8 = (id & 15) * 8;
+            const int64_t grow = rbase + row, gcol = cbase + c8;
+            if (grow >= g.M) continue;
+            const uint4 v = *(const uint4*)(ct + row * 128 + c8);
+            uint16_t* dst = (uint16_t*)g.c + grow * g.ldc + gcol;
+            if (vec && gcol + 8 <= g.N) {
+                *(uint4*)dst = v;
+            } else {
+                const uint16_t* e = (const uint16_t*)&v;
+                for (int k = 0; k < 8; k++)
+                    if (gcol + k < g.N) dst[k] = e[k];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int64_t col = n0 + wn * 128 + j * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                    if (row < g.M && col < g.N) ((float*)g.c)[row * g.ldc + col] = acc[i][j][r] * ap;
+                }
+            }
+    }
+#endif
+}
+
 template <int FA, int FB, int OUT>
 hipError_t launch3(const GArgs& a, hipStream_t s)
 {
     const unsigned nwg = (unsigned)(a.tiles_m * a.tiles_n);
+    if constexpr (FA != E2M1 && FB != E2M1) {
+        if (!a.reg_path && a.K % BKB == 0) {
+            k_gemm_w4<FA, FB, OUT><<<dim3(nwg), dim3(256), 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
     k_gemm<FA, FB, OUT><<<dim3(nwg), dim3(512), 0, s>>>(a);
     return hipGetLastError();
 }

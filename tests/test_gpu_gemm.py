@@ -49,6 +49,11 @@ CASES = [
     ("two_level", "e4m3", "e4m3", 200, 300, 256, "f32", dict(two_level=True)),
     ("two_level_bf16", "e4m3", "e4m3", 512, 512, 512, "bf16", dict(two_level=True)),
     ("tiny", "e4m3", "e4m3", 1, 1, 32, "f32", {}),
+    # FP8 with K a multiple of 128 runs the one-wave-per-SIMD kernel: one
+    # stage, an odd stage count, ragged M and N, bf16 output
+    ("k128_one_stage", "e4m3", "e4m3", 300, 200, 128, "f32", {}),
+    ("e5m2_e4m3_five_stages", "e5m2", "e4m3", 129, 260, 640, "f32", {}),
+    ("e4m3_e5m2_bf16_ragged", "e4m3", "e5m2", 257, 300, 1152, "bf16", {}),
 ]
 
 
@@ -90,9 +95,10 @@ def _alpha_prime(alpha, ta, tb, hk):
     return ap / 32.0 if hk else ap
 
 
-def test_gemm_ldc():
+@pytest.mark.parametrize("K", [64, 256])
+def test_gemm_ldc(K):
     rng = np.random.default_rng(9)
-    M, N, K = 70, 50, 64
+    M, N = 70, 50
     a = rng.standard_normal((M, K)).astype(np.float32)
     b = rng.standard_normal((K, N)).astype(np.float32)
     (qa, sa, _), (qao, sao, _) = quant_both(a, O.AXIS_ROW, "e4m3")
