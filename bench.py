@@ -40,8 +40,8 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0}   # dense scaled MFMA
 # commands are in profiles/.  Keyed by the SHA-256 of the kernel's source
 # file at measurement time: a changed kernel reports null until re-measured.
 MEASURED_TRAFFIC = {
-    "moss": {"source": "gemm.hip", "sha256": "be4f65b6fbcf1ab5",
-             "fetch_kib": 51502.5, "write_kib": 34306.6},
+    "moss": {"source": "gemm.hip", "sha256": "f2b25b139f2ff23e",
+             "fetch_kib": 50949.0, "write_kib": 32768.0},
 }
 
 
@@ -330,7 +330,7 @@ def main():
         peak = MFMA_PEAK_TFLOPS[info["mfma"]]
         roofline = {"bound": "mfma", "achieved": round(g_tf, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(g_tf / peak, 4), "traffic": measured_traffic(args.workload),
-                    "kernel": f"k_gemm ({info['mfma']} scaled MFMA)",
+                    "kernel": f"{'k_gemm_w4' if info['mfma'] == 'fp8' else 'k_gemm'} ({info['mfma']} scaled MFMA)",
                     "algorithmic": f"{info['flops']:.4g} FLOP per launch"}
         value = info["flops"] / (step_ms * 1e-3) / 1e12
         metric = "MX GEMM TFLOP/s (% scaled-MFMA peak); mx_quantize GB/s (% HBM peak)"
