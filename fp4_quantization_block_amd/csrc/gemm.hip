@@ -732,6 +732,9 @@ void k_gemm_w4(GArgs g)
         stSA = uSA;
         stSB = uSB;
     }
+    // stages 2 and 3 warm L2 here; the main loop warms stage s + 4
+    prefetch(min(2, nstages - 1));
+    prefetch(min(3, nstages - 1));
     half_barrier();
 #pragma unroll
     for (int q = 0; q < 8; q++) rd_frag(F0, lA0, lB0, 0, q);
