@@ -103,7 +103,8 @@ def test_quantize_small_all_options(fmt, src, mode, opt):
         assert_same_f32(ts.cpu().numpy(), [st])
 
 
-def test_nonfinite_and_degenerate_blocks():
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_nonfinite_and_degenerate_blocks(src):
     x = np.ones((64, 64), np.float32)
     x[0, 3] = np.nan                      # NaN block (row 0, cols 0-31; col 3, rows 0-31)
     x[33, 40] = -np.inf
@@ -112,6 +113,9 @@ def test_nonfinite_and_degenerate_blocks():
     x[35, :32] = 2.0 ** -149              # smallest fp32 subnormal
     x[36, :32] = 3.4e38                   # near fp32 max
     x[37, :32] = 240.0                    # 1.875 * 2^7: saturates in E4M3
+    x[38, :32] = -250.0                   # rounds past 448 * 2^-1 after scaling: saturates
+    if src == "bf16":                     # bf16 source: the packed-pair encoder for FP8 copies
+        x = I.to_bf16_bits(x)
     for fmt in FMTS:
         for opts in (dict(), dict(sr=True), dict(hadamard=True)):
             row, col, _ = run_gpu(to_device(x), "dual", fmt, opts)
