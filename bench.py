@@ -330,7 +330,7 @@ def main():
         peak = MFMA_PEAK_TFLOPS[info["mfma"]]
         roofline = {"bound": "mfma", "achieved": round(g_tf, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(g_tf / peak, 4), "traffic": measured_traffic(args.workload),
-                    "kernel": f"{'k_gemm_w4' if info['mfma'] == 'fp8' else 'k_gemm'} ({info['mfma']} scaled MFMA)",
+                    "kernel": f"k_gemm_w4 ({info['mfma']} scaled MFMA)",
                     "algorithmic": f"{info['flops']:.4g} FLOP per launch"}
         value = info["flops"] / (step_ms * 1e-3) / 1e12
         metric = "MX GEMM TFLOP/s (% scaled-MFMA peak); mx_quantize GB/s (% HBM peak)"

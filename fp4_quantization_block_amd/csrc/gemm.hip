@@ -571,8 +571,9 @@ __device__ __forceinline__ void pin4(f16v (&acc)[4][4])
 #endif
 }
 
+template <bool FP4>
 struct W4Frag {
-    int8v a[4], b[4];
+    typename KFrag<FP4>::V a[4], b[4];
     uint32_t sa[4], sb[4];
 };
 
@@ -581,12 +582,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_w4(GArgs g)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
+    constexpr bool FP4 = (FA == E2M1);
+    constexpr int EPB = FP4 ? 2 : 1;                 // elements per byte
+    constexpr int KS = BKB * EPB / 64;               // MFMA k-steps per stage (2 FP8, 4 FP4)
+    constexpr int SBD = KS / 2;                      // scale dwords per row per stage
+    typedef W4Frag<FP4> Frag;
     __shared__ __align__(16) uint8_t lA0[TILE_BYTES], lA1[TILE_BYTES];
     __shared__ __align__(16) uint8_t lB0[TILE_BYTES], lB1[TILE_BYTES];
     // scale dwords of a stage, [A rows | B rows], in two planes: plane 1 holds
     // each dword shifted right by one byte, so a lane with h = 1 finds its
     // blocks at bytes 0 and 2 without a shift after the read
-    __shared__ __align__(16) uint32_t lS0[4 * BM], lS1[4 * BM];
+    // (SBD dwords per row per stage: [plane][dword][A rows | B rows])
+    __shared__ __align__(16) uint32_t lS0[2 * SBD * 2 * BM], lS1[2 * SBD * 2 * BM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -597,7 +604,7 @@ void k_gemm_w4(GArgs g)
     int tm, tn;
     tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const int64_t kbytes = g.K;
+    const int64_t kbytes = g.K / EPB;
     const int64_t kblocks = g.K / 32;
     const int nstages = (int)(kbytes / BKB);
 
@@ -622,7 +629,7 @@ void k_gemm_w4(GArgs g)
     const uint32_t wofs = (uint32_t)swz(lr, lc);
 
     uint4 stA[8], stB[8];
-    uint32_t stSA, stSB;
+    uint32_t stSA[SBD], stSB[SBD];
     // L2 warm-up: four stages ahead of its loads, each workgroup touches a
     // share of its A and B rows chosen so that the tiles sharing a panel on
     // one XCD (a block of 4 tile rows x 8 tile columns) touch different
@@ -642,42 +649,58 @@ void k_gemm_w4(GArgs g)
     auto gl16 = [&](__amdgpu_buffer_rsrc_t r, int p, int s) __attribute__((always_inline)) {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + p * prow, s * BKB, 0));
     };
+    auto gload_scales = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int d = 0; d < SBD; d++) {
+            stSA[d] = __builtin_amdgcn_raw_buffer_load_b32(rsa_, vsoff, s * 4 * SBD + 4 * d, 0);
+            stSB[d] = __builtin_amdgcn_raw_buffer_load_b32(rsb_, vsoff, s * 4 * SBD + 4 * d, 0);
+        }
+    };
     auto gload = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < 8; p++) {
             stA[p] = gl16(ra, p, s);
             stB[p] = gl16(rb, p, s);
         }
-        stSA = __builtin_amdgcn_raw_buffer_load_b32(rsa_, vsoff, s * 4, 0);
-        stSB = __builtin_amdgcn_raw_buffer_load_b32(rsb_, vsoff, s * 4, 0);
+        gload_scales(s);
     };
 
     // fragment reads (same lane layout and swizzle as k_gemm)
     const uint32_t oa = (uint32_t)((wm * 128 + l32) * BKB);
     const uint32_t ob = (uint32_t)((wn * 128 + l32) * BKB);
     const uint32_t hk = (uint32_t)((h ^ swz_key(l32)) << 4);
-    const int rsa = 2 * BM * h + wm * 128 + l32, rsb = 2 * BM * h + BM + wn * 128 + l32;
-    // fragment t (0..3: A tile t, 4..7: B tile t-4) of k-step ks
-    auto rd_frag = [&](W4Frag& f, const uint8_t* sA, const uint8_t* sB, int ks, int t) __attribute__((always_inline)) {
-        const uint32_t c0 = ((uint32_t)(ks * 4) << 4) ^ hk, c1 = ((uint32_t)(ks * 4 + 2) << 4) ^ hk;
+    const int rsa = 2 * BM * SBD * h + wm * 128 + l32, rsb = 2 * BM * SBD * h + BM + wn * 128 + l32;
+    // fragment t (0..3: A tile t, 4..7: B tile t-4) of k-step ks: FP8 holds
+    // chunks 4ks + h and 4ks + 2 + h of the lane's row, FP4 chunk 2ks + h
+    auto rd_frag = [&](Frag& f, const uint8_t* sA, const uint8_t* sB, int ks, int t) __attribute__((always_inline)) {
         const uint8_t* base = t < 4 ? sA + oa + (t & 3) * 32 * BKB : sB + ob + (t & 3) * 32 * BKB;
-        const uint4 v0 = *(const uint4*)(base + c0);
-        const uint4 v1 = *(const uint4*)(base + c1);
-        const int8v v = int8v{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        typename KFrag<FP4>::V v;
+        if constexpr (FP4) {
+            const uint4 v0 = *(const uint4*)(base + ((((uint32_t)(ks * 2)) << 4) ^ hk));
+            v = int4v{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w};
+        } else {
+            const uint4 v0 = *(const uint4*)(base + ((((uint32_t)(ks * 4)) << 4) ^ hk));
+            const uint4 v1 = *(const uint4*)(base + ((((uint32_t)(ks * 4 + 2)) << 4) ^ hk));
+            v = int8v{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        }
         if (t < 4) f.a[t] = v;
         else f.b[t - 4] = v;
     };
-    // scale dword of tile t (t < 4: A, else B) with the lane's block of
-    // k-step ks at byte 2 * ks
-    auto rd_scale = [&](W4Frag& f, const uint32_t* sS, int t) __attribute__((always_inline)) {
-        if (t < 4) f.sa[t] = sS[rsa + 32 * t];
-        else f.sb[t - 4] = sS[rsb + 32 * (t - 4)];
+    // scale dword of tile t (t < 4: A, else B) for k-step ks: dword ks / 2
+    // of the stage, with the lane's block at byte 2 * (ks % 2)
+    auto rd_scale = [&](Frag& f, const uint32_t* sS, int t, int ks) __attribute__((always_inline)) {
+        const int d = (ks / 2) * 2 * BM;
+        if (t < 4) f.sa[t] = sS[d + rsa + 32 * t];
+        else f.sb[t - 4] = sS[d + rsb + 32 * (t - 4)];
     };
     auto wr_scales = [&](uint32_t* sS) __attribute__((always_inline)) {
-        sS[tid] = stSA;
-        sS[BM + tid] = stSB;
-        sS[2 * BM + tid] = stSA >> 8;
-        sS[3 * BM + tid] = stSB >> 8;
+#pragma unroll
+        for (int d = 0; d < SBD; d++) {
+            sS[d * 2 * BM + tid] = stSA[d];
+            sS[d * 2 * BM + BM + tid] = stSB[d];
+            sS[(SBD + d) * 2 * BM + tid] = stSA[d] >> 8;
+            sS[(SBD + d) * 2 * BM + BM + tid] = stSB[d] >> 8;
+        }
     };
     auto swrite_a = [&](uint8_t* sA, int p) __attribute__((always_inline)) { *(uint4*)(sA + p * 32 * BKB + wofs) = stA[p]; };
     auto swrite_b = [&](uint8_t* sB, int p) __attribute__((always_inline)) { *(uint4*)(sB + p * 32 * BKB + wofs) = stB[p]; };
@@ -690,18 +713,18 @@ void k_gemm_w4(GArgs g)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-    auto mma = [&](const W4Frag& f, int ks, int m) __attribute__((always_inline)) {
+    auto mma = [&](const Frag& f, int ks, int m) __attribute__((always_inline)) {
         const int i = m >> 2, j = m & 3;
-        if (ks == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], MfmaFmt<FA>::code,
-                                                                        MfmaFmt<FB>::code, 0, (int)f.sa[i], 0, (int)f.sb[j]);
+        if ((ks & 1) == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mfma_src<FP4>(f.a[i]), mfma_src<FP4>(f.b[j]), acc[i][j],
+                                                                        MfmaFmt<FA>::code, MfmaFmt<FB>::code, 0, (int)f.sa[i], 0, (int)f.sb[j]);
         else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], MfmaFmt<FA>::code,
-                                                                        MfmaFmt<FB>::code, 2, (int)f.sa[i], 2, (int)f.sb[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mfma_src<FP4>(f.a[i]), mfma_src<FP4>(f.b[j]), acc[i][j],
+                                                                        MfmaFmt<FA>::code, MfmaFmt<FB>::code, 2, (int)f.sa[i], 2, (int)f.sb[j]);
     };
 
     pin4(acc);
-    W4Frag F0, F1;
+    Frag F0, F1;
     // prologue: stage 0 into buffer 0 and stage 1's A tile into buffer 1;
     // stage 1's B tile and scales, and stage 2's A tile, left in flight
     // (stage 1 is loaded into temporaries before stage 0 is waited for, so
@@ -715,8 +738,12 @@ void k_gemm_w4(GArgs g)
             uA[p] = gl16(ra, p, s1);
             uB[p] = gl16(rb, p, s1);
         }
-        const uint32_t uSA = __builtin_amdgcn_raw_buffer_load_b32(rsa_, vsoff, s1 * 4, 0);
-        const uint32_t uSB = __builtin_amdgcn_raw_buffer_load_b32(rsb_, vsoff, s1 * 4, 0);
+        uint32_t uSA[SBD], uSB[SBD];
+#pragma unroll
+        for (int d = 0; d < SBD; d++) {
+            uSA[d] = __builtin_amdgcn_raw_buffer_load_b32(rsa_, vsoff, s1 * 4 * SBD + 4 * d, 0);
+            uSB[d] = __builtin_amdgcn_raw_buffer_load_b32(rsb_, vsoff, s1 * 4 * SBD + 4 * d, 0);
+        }
 #pragma unroll
         for (int p = 0; p < 8; p++) {
             swrite_a(lA0, p);
@@ -729,8 +756,11 @@ void k_gemm_w4(GArgs g)
             *(uint4*)(lA1 + p * 32 * BKB + wofs) = uA[p];
             stB[p] = uB[p];
         }
-        stSA = uSA;
-        stSB = uSB;
+#pragma unroll
+        for (int d = 0; d < SBD; d++) {
+            stSA[d] = uSA[d];
+            stSB[d] = uSB[d];
+        }
     }
     // stages 2 and 3 warm L2 here; the main loop warms stage s + 4
     prefetch(min(2, nstages - 1));
@@ -739,55 +769,67 @@ void k_gemm_w4(GArgs g)
 #pragma unroll
     for (int q = 0; q < 8; q++) rd_frag(F0, lA0, lB0, 0, q);
 #pragma unroll
-    for (int t = 0; t < 8; t++) rd_scale(F0, lS0, t);
+    for (int t = 0; t < 8; t++) rd_scale(F0, lS0, t, 0);
 
     // Stage s computes from buffer X and fills buffer Y with stage s+1 and
-    // X with stage s+2.  The LDS writes are split between the phases so
-    // that neither carries all of them: phase A writes stage s+1's B tile
-    // and scales to Y (the A tile went there in phase B of stage s-1) and
-    // reloads them with stage s+2; phase B, after the barrier that ends
-    // every read of X, writes stage s+2's A tile to X and reloads it with
-    // stage s+3.  Each register-held tile thus has a whole stage to arrive.
-    auto stage = [&](int s, uint8_t* xA, uint8_t* xB, uint32_t* xS, uint8_t* yA, uint8_t* yB,
-                     uint32_t* yS) __attribute__((always_inline)) {
+    // X with stage s+2.  Each k-step is a phase of 16 MFMAs from one
+    // fragment set while the other set is read for the next k-step (the
+    // sets alternate with the k-step's parity).  The barrier comes before
+    // the last phase, which reads the next stage's first k-step from Y.
+    // The LDS writes are split so that no phase carries all of them: the
+    // first phase writes stage s+1's B tile to Y (its A tile went there in
+    // the last phase of stage s-1) and reloads it with stage s+2, the
+    // second writes the scales; the last phase, after the barrier that
+    // ends every read of X, writes stage s+2's A tile to X and reloads it
+    // with stage s+3.  Each register-held tile has a whole stage to arrive.
+    auto phase = [&](auto KSC, int s, Frag& cur, Frag& nxt, uint8_t* xA, const uint8_t* xB, const uint32_t* xS,
+                     uint8_t* yA, uint8_t* yB, uint32_t* yS) __attribute__((always_inline)) {
+        constexpr int ks = decltype(KSC)::value;
+        constexpr bool last = ks == KS - 1;
         const int s2 = min(s + 2, nstages - 1), s3 = min(s + 3, nstages - 1);
-        // phase A
 #pragma unroll
         for (int m = 0; m < 16; m++) {
-            mma(F0, 0, m);
+            mma(cur, ks, m);
             __builtin_amdgcn_sched_barrier(0);
             if (m < 8) {
-                rd_frag(F1, xA, xB, 1, m);
-                swrite_b(yB, m);
-                stB[m] = gl16(rb, m, s2);
+                if constexpr (last) rd_frag(nxt, yA, yB, 0, m);
+                else rd_frag(nxt, xA, xB, ks + 1, m);
             } else {
-                rd_scale(F1, xS, m - 8);
+                if constexpr (last) rd_scale(nxt, yS, m - 8, 0);
+                else rd_scale(nxt, xS, m - 8, ks + 1);
+            }
+            if constexpr (ks == 0) {
+                if (m < 8) {
+                    swrite_b(yB, m);
+                    stB[m] = gl16(rb, m, s2);
+                }
                 if (m == 9) prefetch(min(s + 4, nstages - 1));
+            }
+            if constexpr (ks == (KS == 2 ? 0 : 1)) {
                 if (m == 8) {
                     wr_scales(yS);
-                    stSA = __builtin_amdgcn_raw_buffer_load_b32(rsa_, vsoff, s2 * 4, 0);
-                    stSB = __builtin_amdgcn_raw_buffer_load_b32(rsb_, vsoff, s2 * 4, 0);
+                    gload_scales(s2);
+                }
+            }
+            if constexpr (last) {
+                if (m >= 8) {
+                    swrite_a(xA, m - 8);
+                    stA[m - 8] = gl16(ra, m - 8, s3);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         pin4(acc);
-        half_barrier();
-        // phase B
-#pragma unroll
-        for (int m = 0; m < 16; m++) {
-            mma(F1, 1, m);
-            __builtin_amdgcn_sched_barrier(0);
-            if (m < 8) {
-                rd_frag(F0, yA, yB, 0, m);
-            } else {
-                rd_scale(F0, yS, m - 8);
-                swrite_a(xA, m - 8);
-                stA[m - 8] = gl16(ra, m - 8, s3);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ks == KS - 2) half_barrier();
+    };
+    auto stage = [&](int s, uint8_t* xA, uint8_t* xB, uint32_t* xS, uint8_t* yA, uint8_t* yB,
+                     uint32_t* yS) __attribute__((always_inline)) {
+        phase(std::integral_constant<int, 0>{}, s, F0, F1, xA, xB, xS, yA, yB, yS);
+        phase(std::integral_constant<int, 1>{}, s, F1, F0, xA, xB, xS, yA, yB, yS);
+        if constexpr (KS == 4) {
+            phase(std::integral_constant<int, 2>{}, s, F0, F1, xA, xB, xS, yA, yB, yS);
+            phase(std::integral_constant<int, 3>{}, s, F1, F0, xA, xB, xS, yA, yB, yS);
         }
-        pin4(acc);
     };
     for (int s = 0; s < nstages; s += 2) {
         stage(s, lA0, lB0, lS0, lA1, lB1, lS1);
@@ -857,11 +899,10 @@ template <int FA, int FB, int OUT>
 hipError_t launch3(const GArgs& a, hipStream_t s)
 {
     const unsigned nwg = (unsigned)(a.tiles_m * a.tiles_n);
-    if constexpr (FA != E2M1 && FB != E2M1) {
-        if (!a.reg_path && a.K % BKB == 0) {
-            k_gemm_w4<FA, FB, OUT><<<dim3(nwg), dim3(256), 0, s>>>(a);
-            return hipGetLastError();
-        }
+    constexpr int EPB = FA == E2M1 ? 2 : 1;
+    if (!a.reg_path && (a.K / EPB) % BKB == 0) {
+        k_gemm_w4<FA, FB, OUT><<<dim3(nwg), dim3(256), 0, s>>>(a);
+        return hipGetLastError();
     }
     k_gemm<FA, FB, OUT><<<dim3(nwg), dim3(512), 0, s>>>(a);
     return hipGetLastError();

@@ -54,6 +54,9 @@ CASES = [
     ("k128_one_stage", "e4m3", "e4m3", 300, 200, 128, "f32", {}),
     ("e5m2_e4m3_five_stages", "e5m2", "e4m3", 129, 260, 640, "f32", {}),
     ("e4m3_e5m2_bf16_ragged", "e4m3", "e5m2", 257, 300, 1152, "bf16", {}),
+    # FP4 with K a multiple of 256 runs it too (four k-steps per stage)
+    ("e2m1_three_stages_ragged", "e2m1", "e2m1", 300, 280, 768, "f32", {}),
+    ("e2m1_one_stage_bf16", "e2m1", "e2m1", 257, 200, 256, "bf16", dict(hadamard=True)),
 ]
 
 
