@@ -61,6 +61,11 @@ def _load():
     L.or_tensor_amax.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64]
     L.or_tensor_scale.restype = ctypes.c_float
     L.or_tensor_scale.argtypes = [ctypes.c_int, ctypes.c_float]
+    L.or_predict_max.restype = ctypes.c_float
+    L.or_predict_max.argtypes = [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.c_float]
+    L.or_predict_tensor_scale.restype = ctypes.c_float
+    L.or_predict_tensor_scale.argtypes = [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.c_float,
+                                          ctypes.c_int]
     L.or_round_bf16.restype = ctypes.c_double
     L.or_round_bf16.argtypes = [ctypes.c_double]
     L.or_quantize_block.restype = ctypes.c_uint
@@ -169,6 +174,27 @@ def tensor_amax(x):
 
 def tensor_scale(fmt, amax):
     return _load().or_tensor_scale(_fmt(fmt), float(amax))
+
+
+def _pair(w, g):
+    w, g = np.ascontiguousarray(w), np.ascontiguousarray(g)
+    if w.shape != g.shape or w.dtype != g.dtype:
+        raise ValueError("w and g must have the same shape and dtype")
+    return w, g
+
+
+def predict_max(w, g, lr):
+    """[MOSS, "创新 2：权重自动缩放"]: max|W| + lr*max|g| in fp32 (product, then sum)."""
+    w, g = _pair(w, g)
+    return _load().or_predict_max(_ptr(w), _ptr(g), _src(w), w.shape[0], w.shape[1], w.shape[1],
+                                  g.shape[1], float(lr))
+
+
+def predict_tensor_scale(w, g, lr, fmt):
+    """Predicted per-tensor scale of the next step's weights: predict_max / Fmax."""
+    w, g = _pair(w, g)
+    return _load().or_predict_tensor_scale(_ptr(w), _ptr(g), _src(w), w.shape[0], w.shape[1],
+                                           w.shape[1], g.shape[1], float(lr), _fmt(fmt))
 
 
 def round_bf16(x):

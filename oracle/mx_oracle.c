@@ -240,6 +240,30 @@ float or_tensor_scale(int fmt, float amax)
     return amax / fmax;                        /* one IEEE binary32 division */
 }
 
+/* [MOSS, "创新 2：权重自动缩放"]: an update W' = W - lr*g moves no element
+ * by more than lr*max|g|, so max|W'| <= max|W| + lr*max|g|.  The predicted
+ * max is that sum, in fp32 as written: one product, then one sum (no fused
+ * multiply-add); NaN if either tensor holds a NaN. */
+float or_predict_max(const void* w, const void* g, int src, int64_t rows, int64_t cols,
+                     int64_t ld_w, int64_t ld_g, float lr)
+{
+    const float aw = or_tensor_amax(w, src, rows, cols, ld_w);
+    const float ag = or_tensor_amax(g, src, rows, cols, ld_g);
+    if (isnan(aw) || isnan(ag)) return NAN;
+    const float step = lr * ag;
+    return aw + step;
+}
+
+/* the per-tensor scale of the next step's weights: predicted max / Fmax,
+ * the same division (and the same unit scale for zero) as a computed
+ * two-level scale.  The page divides by 127 for its int8 illustration;
+ * Fmax of the element format is the FP8/FP4 reading. */
+float or_predict_tensor_scale(const void* w, const void* g, int src, int64_t rows, int64_t cols,
+                              int64_t ld_w, int64_t ld_g, float lr, int fmt)
+{
+    return or_tensor_scale(fmt, or_predict_max(w, g, src, rows, cols, ld_w, ld_g, lr));
+}
+
 double or_round_bf16(double x)
 {
     /* nearest bfloat16 (8 significant bits, fp32 exponent range), ties to

@@ -49,6 +49,11 @@ void  or_fwht32(float v[32]);
 float or_tensor_amax(const void* x, int src, int64_t rows, int64_t cols, int64_t ld);
 float or_tensor_scale(int fmt, float amax);
 double or_round_bf16(double x);
+/* weight auto-scaling: predicted max|W - lr*g| bound and the scale from it */
+float or_predict_max(const void* w, const void* g, int src, int64_t rows, int64_t cols,
+                     int64_t ld_w, int64_t ld_g, float lr);
+float or_predict_tensor_scale(const void* w, const void* g, int src, int64_t rows, int64_t cols,
+                              int64_t ld_w, int64_t ld_g, float lr, int fmt);
 
 /* ---- one block ----
  * v: the 32 values of the block after the optional two-level division and

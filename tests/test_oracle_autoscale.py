@@ -1,0 +1,90 @@
+"""Pins of the oracle's weight auto-scaling ([MOSS, "创新 2：权重自动缩放"]):
+the predicted max max|W| + lr*max|g| and the per-tensor scale from it.
+
+What fixes the function, other than its own formula:
+  * the page's bound: an update W' = W - lr*g (fp32, product then
+    difference) never exceeds the predicted max -- exactly, since IEEE
+    rounding is monotone;
+  * tightness: with the two maxima at one index and opposite signs the
+    update reaches the predicted max bit for bit;
+  * lr = 0 reduces the prediction to the computed two-level scale of W;
+  * zeros, NaN and Inf follow the computed scale's special cases.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from fp4_quantization_block_amd import inputs as I
+
+FMTS = ["e4m3", "e5m2", "e2m1"]
+FMAX = {"e4m3": 448.0, "e5m2": 57344.0, "e2m1": 6.0}
+
+
+def _pair(rng, rows, cols, src, wscale=0.02, gscale=1e-3):
+    w = (rng.standard_normal((rows, cols)) * wscale).astype(np.float32)
+    g = (rng.laplace(0.0, gscale, (rows, cols))).astype(np.float32)
+    if src == "bf16":
+        return I.to_bf16_bits(w), I.to_bf16_bits(g)
+    return w, g
+
+
+def _f32(x):
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+@pytest.mark.parametrize("lr", [0.0, 1e-4, 3e-3, 0.1, 1.0, 7.5])
+def test_update_never_exceeds_predicted_max(src, lr):
+    rng = np.random.default_rng(int(lr * 1e4) + (src == "bf16"))
+    for rows, cols in [(1, 1), (3, 70), (64, 96), (257, 33)]:
+        w, g = _pair(rng, rows, cols, src)
+        p = np.float32(O.predict_max(w, g, lr))
+        wf, gf = _f32(w), _f32(g)
+        upd = wf - np.float32(lr) * gf                  # fp32: product rounded, then difference
+        assert upd.dtype == np.float32
+        assert np.abs(upd).max() <= p, (rows, cols, float(np.abs(upd).max()), float(p))
+
+
+@pytest.mark.parametrize("lr", [1e-3, 0.37, 2.0])
+def test_prediction_is_tight(lr):
+    rng = np.random.default_rng(5)
+    w, g = _pair(rng, 48, 64, "f32")
+    i, j = 17, 40
+    w[i, j] = np.float32(0.5) + np.abs(w).max()        # the largest |W| ...
+    g[i, j] = -(np.float32(1.0) + np.abs(g).max())     # ... and the largest |g| with opposite sign
+    upd = w - np.float32(lr) * g
+    assert np.float32(O.predict_max(w, g, lr)) == np.abs(upd).max()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_zero_lr_is_the_computed_two_level_scale(fmt):
+    rng = np.random.default_rng(7)
+    for src in ("f32", "bf16"):
+        w, g = _pair(rng, 40, 96, src)
+        s = np.float32(O.predict_tensor_scale(w, g, 0.0, fmt))
+        assert s == np.float32(np.abs(_f32(w)).max()) / np.float32(FMAX[fmt])
+        _, _, st = O.quantize(w, O.AXIS_ROW, fmt, two_level=1)
+        assert s == np.float32(st)
+
+
+def test_special_values():
+    z = np.zeros((32, 32), np.float32)
+    assert O.predict_tensor_scale(z, z, 0.5, "e4m3") == 1.0          # all zero: unit scale
+    w = np.full((32, 32), 0.25, np.float32)
+    assert np.float32(O.predict_tensor_scale(w, z, 0.5, "e4m3")) == np.float32(0.25) / np.float32(448)
+    g = z.copy()
+    g[3, 4] = np.nan
+    assert np.isnan(O.predict_tensor_scale(w, g, 0.5, "e4m3"))
+    wi = w.copy()
+    wi[0, 0] = np.inf
+    assert O.predict_tensor_scale(wi, z, 0.5, "e4m3") == np.inf
+    # a provided scale from the prediction quantizes like any provided scale
+    rng = np.random.default_rng(9)
+    w2, g2 = _pair(rng, 32, 64, "f32")
+    s = O.predict_tensor_scale(w2, g2, 1e-2, "e4m3")
+    q1, s1, st = O.quantize(w2, O.AXIS_ROW, "e4m3", two_level=2, tensor_scale=s)
+    assert np.float32(st) == np.float32(s)
+    q2, s2, _ = O.quantize((w2 / np.float32(s)).astype(np.float32), O.AXIS_ROW, "e4m3")
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
