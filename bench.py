@@ -137,6 +137,33 @@ def setup_dual(args):
     return step, info
 
 
+def setup_autoscale(args):
+    """MOSS weight auto-scaling: the next step's per-tensor scale predicted
+    from this step's weight W and gradient G (one read of each), then the
+    updated weight W - lr*G quantized to its column copy with that scale
+    provided -- no amax pass over the new weight."""
+    w = I.make("moss_weight_autoscale_4096")
+    W, G = to_dev(w.tensors["W"]), to_dev(w.tensors["G"])
+    lr = w.meta["lr"]
+    K, N = W.shape
+    W2 = (W.float() - lr * G.float()).to(torch.bfloat16)       # the update (not timed)
+    work = torch.empty(int(mx.load().mx_predict_workspace_bytes()), dtype=torch.uint8, device="cuda")
+    s = torch.empty(1, dtype=torch.float32, device="cuda")
+    cfg = mx.qconfig("e4m3", two_level=True, tscale_provided=True)
+    q = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((N, K // 32), dtype=torch.uint8, device="cuda")
+
+    def step(t):
+        t.run("predict", lambda: mx.mx_predict_tensor_scale(W, G, lr, "e4m3", work=work, scale_out=s))
+        t.run("quant_W", lambda: mx.mx_quantize(W2, mx.MX_AXIS_COL, cfg, q, sc, tensor_scale=s))
+
+    info = dict(flops=0.0, qbytes={"predict": 2 * 2 * K * N, "quant_W": 2 * K * N + K * N + K * N // 32},
+                gemm_kernel=None, mfma=None,
+                config={"workload": "moss_weight_autoscale_e4m3_4096", "K": K, "N": N, "lr": lr},
+                host=w.tensors)
+    return step, info
+
+
 def setup_fp4(args):
     w = I.make("mxfp4_wgrad_qkv")
     dY = to_dev(w.tensors["dY"])          # [T][Q]
@@ -239,7 +266,7 @@ def setup_copy(args):
 
 
 WORKLOADS = {"moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4, "llama": setup_llama,
-             "copy": setup_copy}
+             "copy": setup_copy, "autoscale": setup_autoscale}
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -349,7 +376,8 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic(args.workload),
-                    "kernel": "k_quant dual layout"}
+                    "kernel": {"dual": "k_quant_tile_dma (dual layout)",
+                               "autoscale": "k_amax_partial x2 + k_predict_scale"}.get(args.workload, n)}
         value = gbs
         metric = "mx_quantize GB/s (% HBM peak)"
         unit = "GB/s"

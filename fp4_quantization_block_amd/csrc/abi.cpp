@@ -133,6 +133,31 @@ mx_status mx_quantize_dual_layout(const void* x, int32_t src_dtype, int64_t rows
     return hip_status(mx::launch_quantize(j, (hipStream_t)stream));
 }
 
+int64_t mx_predict_workspace_bytes(void) { return 4096; }
+
+mx_status mx_predict_tensor_scale(const void* w, int64_t ld_w, const void* g, int64_t ld_g,
+                                  int32_t src_dtype, int64_t rows, int64_t cols, float lr,
+                                  int32_t fmt, void* work, int64_t work_bytes, float* scale_out,
+                                  void* stream)
+{
+    g_msg[0] = '\0';
+    mx_status s = check_source(w, src_dtype, rows, cols, ld_w);
+    if (s != MX_OK) return s;
+    if ((s = check_source(g, src_dtype, rows, cols, ld_g)) != MX_OK) return s;
+    if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "unknown element format");
+    if (!(lr >= 0.0f) || lr > 3.4028234663852886e38f) return fail(MX_ERR_INVALID_ARG, "lr must be finite and >= 0");
+    if (!work || !scale_out) return fail(MX_ERR_INVALID_ARG, "work and scale_out must not be NULL");
+    if (work_bytes < mx_predict_workspace_bytes()) return fail(MX_ERR_INVALID_ARG, "work is smaller than mx_predict_workspace_bytes()");
+    if (((reinterpret_cast<uintptr_t>(work) | reinterpret_cast<uintptr_t>(scale_out)) & 3u) != 0)
+        return fail(MX_ERR_ALIGNMENT, "work and scale_out must be 4-byte aligned");
+    mx::PredictJob j{};
+    j.w = w; j.g = g; j.src = src_dtype;
+    j.rows = rows; j.cols = cols; j.ld_w = ld_w; j.ld_g = ld_g;
+    j.lr = lr; j.fmt = fmt;
+    j.work = (uint32_t*)work; j.scale_out = scale_out;
+    return hip_status(mx::launch_predict(j, (hipStream_t)stream));
+}
+
 mx_status mx_gemm(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,
                   const void* qb, const uint8_t* sb, const float* tb, int32_t fb,
                   int64_t M, int64_t N, int64_t K, float alpha, int32_t hadamard_k,

@@ -23,6 +23,19 @@ struct QuantJob {
 
 hipError_t launch_quantize(const QuantJob& j, hipStream_t stream);
 
+// predicted per-tensor scale from W and g (weight auto-scaling)
+struct PredictJob {
+    const void* w; const void* g;
+    int src;                // SRC_F32 / SRC_BF16
+    int64_t rows, cols, ld_w, ld_g;
+    float lr;
+    int fmt;
+    uint32_t* work;         // >= 1024 words of caller workspace
+    float* scale_out;
+};
+
+hipError_t launch_predict(const PredictJob& j, hipStream_t stream);
+
 struct DequantJob {
     const uint8_t* q; const uint8_t* scales; const float* tensor_scale;
     int fmt; int64_t rows, cols; int axis; bool hadamard;

@@ -741,12 +741,12 @@ __device__ __forceinline__ uint32_t key1(const void* x, int64_t i)
 // finite value).  Dense 16-byte-aligned tensors are read as a flat run of
 // 16-byte words with several loads in flight; other layouts row by row.
 template <int SRC>
-__global__ __launch_bounds__(256) void k_amax_partial(const void* x, int64_t rows, int64_t cols,
-                                                      int64_t ld, int flat16, uint32_t* partial)
+__device__ __forceinline__ void amax_partial(const void* x, int64_t rows, int64_t cols, int64_t ld, int flat16,
+                                             uint32_t* partial, int bid, int nblk)
 {
     uint32_t key = 0;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)nblk * blockDim.x;
+    const int64_t t0 = (int64_t)bid * blockDim.x + threadIdx.x;
     if (flat16) {
         constexpr int EPW = SRC == SRC_BF16 ? 8 : 4;
         const int64_t nw = rows * cols / EPW;            // whole 16-byte words
@@ -762,7 +762,7 @@ __global__ __launch_bounds__(256) void k_amax_partial(const void* x, int64_t row
         for (; i < nw; i += stride) key = max(key, key16<SRC>(p[i]));
         for (int64_t e = nw * EPW + t0; e < rows * cols; e += stride) key = max(key, key1<SRC>(x, e));
     } else {
-        for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
+        for (int64_t r = bid; r < rows; r += nblk)
             for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) key = max(key, key1<SRC>(x, r * ld + c));
     }
 #pragma unroll
@@ -770,7 +770,26 @@ __global__ __launch_bounds__(256) void k_amax_partial(const void* x, int64_t row
     __shared__ uint32_t red[4];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = key;
     __syncthreads();
-    if (threadIdx.x == 0) partial[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (threadIdx.x == 0) partial[bid] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+template <int SRC>
+__global__ __launch_bounds__(256) void k_amax_partial(const void* x, int64_t rows, int64_t cols,
+                                                      int64_t ld, int flat16, uint32_t* partial)
+{
+    amax_partial<SRC>(x, rows, cols, ld, flat16, partial, blockIdx.x, gridDim.x);
+}
+
+// partial maxima of two same-shaped tensors in one launch: workgroups
+// [0, n0) take x0 into p0, the rest x1 into p1
+template <int SRC>
+__global__ __launch_bounds__(256) void k_amax_partial2(const void* x0, int64_t ld0, int flat0, uint32_t* p0, int n0,
+                                                       const void* x1, int64_t ld1, int flat1, uint32_t* p1,
+                                                       int64_t rows, int64_t cols)
+{
+    const int b = blockIdx.x;
+    if (b < n0) amax_partial<SRC>(x0, rows, cols, ld0, flat0, p0, b, n0);
+    else amax_partial<SRC>(x1, rows, cols, ld1, flat1, p1, b - n0, gridDim.x - n0);
 }
 
 // One workgroup: s_t from the partial keys, written to the tensor-scale word
@@ -786,6 +805,47 @@ __global__ __launch_bounds__(256) void k_amax_reduce(const uint32_t* partial, in
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = key;
     __syncthreads();
     if (threadIdx.x == 0) *ts = tensor_scale_from_key<FMT>(max(max(red[0], red[1]), max(red[2], red[3])));
+}
+
+// MOSS weight auto-scaling ([MOSS, "创新 2：权重自动缩放"]): one workgroup
+// reduces the partial maxima of W and of g and writes the predicted scale
+// (max|W| + lr * max|g|) / Fmax -- product, sum and division each rounded
+// once in fp32, as written; contraction is switched off so the compiler
+// cannot fuse the product into the sum (HIP contracts by default, which
+// changes the last bit).  NaN when either tensor holds one.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_predict_scale(const uint32_t* pw, int nw, const uint32_t* pg, int ng,
+                                                       float lr, float* out)
+{
+    uint32_t kw = 0, kg = 0;
+    for (int i = threadIdx.x; i < nw; i += blockDim.x) kw = max(kw, pw[i]);
+    for (int i = threadIdx.x; i < ng; i += blockDim.x) kg = max(kg, pg[i]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        kw = max(kw, (uint32_t)__shfl_xor((int)kw, m));
+        kg = max(kg, (uint32_t)__shfl_xor((int)kg, m));
+    }
+    __shared__ uint32_t red[2][4];
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = kw;
+        red[1][threadIdx.x >> 6] = kg;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        kw = max(max(red[0][0], red[0][1]), max(red[0][2], red[0][3]));
+        kg = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+        if (kw > 0x7F800000u || kg > 0x7F800000u) {
+            *out = __uint_as_float(0x7FC00000u);
+            return;
+        }
+        float pmax;
+        {
+#pragma clang fp contract(off)
+            const float step = lr * __uint_as_float(kg);
+            pmax = __uint_as_float(kw) + step;
+        }
+        *out = tensor_scale_from_key<FMT>(__float_as_uint(pmax));
+    }
 }
 
 // persistent grid: as many workgroups as stay resident together (at most 4
@@ -872,6 +932,36 @@ hipError_t launch_fmt(const QuantJob& j, hipStream_t stream)
 }
 
 }  // namespace
+
+template <int SRC, int FMT>
+hipError_t launch_predict_t(const PredictJob& j, hipStream_t stream)
+{
+    // partial maxima of W in work[0, 512), of g in work[512, 1024)
+    constexpr int es = SrcT<SRC>::bytes;
+    int n[2], flat[2];
+    const void* src[2] = {j.w, j.g};
+    const int64_t ld[2] = {j.ld_w, j.ld_g};
+    for (int t = 0; t < 2; t++) {
+        flat[t] = ((reinterpret_cast<uintptr_t>(src[t]) & 15u) == 0) && ld[t] == j.cols && (j.cols * es) % 16 == 0;
+        const int64_t nwords = j.rows * j.cols * es / 16;
+        int64_t want = flat[t] ? (nwords + 2047) / 2048 : j.rows;
+        n[t] = (int)(want < 1 ? 1 : (want > 512 ? 512 : want));
+    }
+    k_amax_partial2<SRC><<<dim3((unsigned)(n[0] + n[1])), dim3(256), 0, stream>>>(
+        j.w, j.ld_w, flat[0], j.work, n[0], j.g, j.ld_g, flat[1], j.work + 512, j.rows, j.cols);
+    k_predict_scale<FMT><<<dim3(1), dim3(256), 0, stream>>>(j.work, n[0], j.work + 512, n[1], j.lr, j.scale_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_predict(const PredictJob& j, hipStream_t stream)
+{
+    const bool bf = j.src == SRC_BF16;
+    switch (j.fmt) {
+    case E4M3: return bf ? launch_predict_t<SRC_BF16, E4M3>(j, stream) : launch_predict_t<SRC_F32, E4M3>(j, stream);
+    case E5M2: return bf ? launch_predict_t<SRC_BF16, E5M2>(j, stream) : launch_predict_t<SRC_F32, E5M2>(j, stream);
+    default:   return bf ? launch_predict_t<SRC_BF16, E2M1>(j, stream) : launch_predict_t<SRC_F32, E2M1>(j, stream);
+    }
+}
 
 hipError_t launch_quantize(const QuantJob& j, hipStream_t stream)
 {

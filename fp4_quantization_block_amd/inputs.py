@@ -84,9 +84,13 @@ FULL_SHAPES = {
     "llama3_8b_mlp": {"T": 8192, "H": 4096, "F": 14336},
     "mxfp4_wgrad_qkv": {"T": 16384, "H": 4096, "Q": 6144},
     "dual_layout_16384x14336": {"R": 16384, "C": 14336},
+    # MOSS weight auto-scaling on the 4096x4096 weight of the two-level
+    # workload: this step's weights and gradient, and the page's lr
+    "moss_weight_autoscale_4096": {"K": 4096, "N": 4096},
 }
 WORKLOAD_SEEDS = {"mxfp8_gemm_256": 1, "moss_two_level_4096": 2, "llama3_8b_mlp": 3,
-                  "mxfp4_wgrad_qkv": 4, "dual_layout_16384x14336": 5}
+                  "mxfp4_wgrad_qkv": 4, "dual_layout_16384x14336": 5,
+                  "moss_weight_autoscale_4096": 6}
 
 
 def make(name: str, **shape_override) -> Workload:
@@ -119,6 +123,11 @@ def make(name: str, **shape_override) -> Workload:
     elif name == "dual_layout_16384x14336":
         R, C = shp["R"], shp["C"]
         w.tensors["X"] = to_bf16_bits(normal_with_outlier_elements(seed, 0, (R, C)))
+    elif name == "moss_weight_autoscale_4096":
+        K, N = shp["K"], shp["N"]
+        w.tensors["W"] = to_bf16_bits(normal(seed, 0, (K, N), std=0.02))     # like the MOSS weight B
+        w.tensors["G"] = to_bf16_bits(normal(seed, 1, (K, N), std=1e-3))     # like the MLP gradients
+        w.meta["lr"] = 1e-3
     else:
         raise KeyError(name)
     return w

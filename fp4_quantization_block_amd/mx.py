@@ -25,7 +25,8 @@ MX_OUT_F32, MX_OUT_BF16 = 0, 1
 
 FMTS = {"e4m3": MX_E4M3, "e5m2": MX_E5M2, "e2m1": MX_E2M1}
 EXPORTED = ("mx_quantize", "mx_quantize_dual_layout", "mx_gemm", "mx_dequantize",
-            "mx_status_string", "mx_last_error_message")
+            "mx_status_string", "mx_last_error_message",
+            "mx_predict_tensor_scale", "mx_predict_workspace_bytes")
 
 
 class MXError(RuntimeError):
@@ -66,6 +67,11 @@ def load() -> ctypes.CDLL:
                           ctypes.c_float, _i32, _vp, _i32, _i64, _vp]
     L.mx_dequantize.restype = _i32
     L.mx_dequantize.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i32, _i32, _vp, _i32, _vp]
+    L.mx_predict_tensor_scale.restype = _i32
+    L.mx_predict_tensor_scale.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, ctypes.c_float, _i32,
+                                          _vp, _i64, _vp, _vp]
+    L.mx_predict_workspace_bytes.restype = _i64
+    L.mx_predict_workspace_bytes.argtypes = []
     L.mx_status_string.restype = ctypes.c_char_p
     L.mx_status_string.argtypes = [_i32]
     L.mx_last_error_message.restype = ctypes.c_char_p
@@ -180,6 +186,25 @@ def mx_gemm(qa, sa, ta, fa, qb, sb, tb, fb, M: int, N: int, K: int, alpha: float
                           _fmt(fb), M, N, K, float(alpha), int(bool(hadamard_k)), _ptr(c),
                           out_dtype, ldc, _stream(stream)))
     return c
+
+
+def mx_predict_tensor_scale(w: torch.Tensor, g: torch.Tensor, lr: float, fmt,
+                            work: Optional[torch.Tensor] = None, scale_out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """Predicted per-tensor scale of the next step's weights (weight auto-scaling)."""
+    src = _src(w)
+    if _src(g) != src or tuple(g.shape) != tuple(w.shape):
+        raise ValueError("w and g must have the same dtype and shape")
+    rows, cols = w.shape
+    nbytes = int(load().mx_predict_workspace_bytes())
+    if work is None:
+        work = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    if scale_out is None:
+        scale_out = torch.empty(1, dtype=torch.float32, device=w.device)
+    _check(load().mx_predict_tensor_scale(_ptr(w), w.stride(0), _ptr(g), g.stride(0), src, rows, cols,
+                                          float(lr), _fmt(fmt), _ptr(work), work.numel() * work.element_size(),
+                                          _ptr(scale_out), _stream(stream)))
+    return scale_out
 
 
 def mx_dequantize(q, scales, tensor_scale, fmt, rows: int, cols: int, axis: int,

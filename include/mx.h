@@ -180,6 +180,40 @@ mx_status mx_dequantize(const void* q, const uint8_t* scales, const float* tenso
                         int32_t fmt, int64_t rows, int64_t cols, int32_t axis, int32_t hadamard,
                         void* out, int32_t out_dtype, void* stream);
 
+/*
+ * mx_predict_tensor_scale -- MOSS weight auto-scaling ([MOSS, "创新 2：权重
+ * 自动缩放"]): the per-tensor scale of the NEXT step's weights, predicted
+ * from this step's weights W and update direction g without a pass over
+ * the updated weights.  An update W' = W - lr*g moves no element by more
+ * than lr*max|g|, so max|W'| <= max|W| + lr*max|g| (exactly, also in fp32
+ * arithmetic: rounding is monotone), and
+ *     scale_out = RN(RN(max|W| + RN(lr * max|g|)) / Fmax(fmt))
+ * -- product, sum and IEEE division each rounded once, in that order
+ * (the page's int8 illustration divides by 127; Fmax is 448 / 57344 / 6).
+ * 1 when the sum is 0; NaN when W or g holds a NaN; +Inf when one holds
+ * an Inf.  Pass the result to mx_quantize / mx_quantize_dual_layout with
+ * MX_SCALE_E8M0_TENSOR_F32 and MX_TSCALE_PROVIDED for W'.
+ *
+ * w, g:   device tensors of `src_dtype`, both rows x cols, row strides
+ *         ld_w, ld_g >= cols elements, aligned to the element size.  g is
+ *         the direction the step subtracts (the gradient for the page's
+ *         W - lr*gradient form).
+ * lr:     finite, >= 0.
+ * work:   caller-owned device workspace of at least
+ *         mx_predict_workspace_bytes() bytes, 4-byte aligned; it holds the
+ *         partial maxima, and its contents are undefined afterwards.
+ * scale_out: one fp32 in device memory, 4-byte aligned.
+ * Errors: MX_ERR_INVALID_ARG (null pointers, bad dtype/format, shapes,
+ *         lr, small workspace), MX_ERR_ALIGNMENT, MX_ERR_HIP.
+ */
+mx_status mx_predict_tensor_scale(const void* w, int64_t ld_w, const void* g, int64_t ld_g,
+                                  int32_t src_dtype, int64_t rows, int64_t cols, float lr,
+                                  int32_t fmt, void* work, int64_t work_bytes, float* scale_out,
+                                  void* stream);
+
+/* Bytes of workspace mx_predict_tensor_scale needs (a constant, 4096). */
+int64_t mx_predict_workspace_bytes(void);
+
 /* Static text for a status code. */
 const char* mx_status_string(mx_status status);
 

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "mx.h")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:mx_status|const char\*)\s+(mx_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:mx_status|const char\*|int64_t)\s+(mx_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -124,3 +124,38 @@ def test_dequantize_validation(lib):
     assert f(FAKE, FAKE, None, 0, 40, 64, 1, 0, FAKE, 0, None) == mx.MX_ERR_INVALID_ARG
     assert f(FAKE, FAKE, None, 0, 64, 64, 0, 0, FAKE_ODD, 0, None) == mx.MX_ERR_ALIGNMENT
     assert f(FAKE, FAKE, None, 0, 64, 64, 0, 3, FAKE, 0, None) == mx.MX_ERR_INVALID_ARG
+
+
+def _predict(lib, w=None, ldw=64, g=None, ldg=64, src=1, rows=64, cols=64, lr=1e-3, fmt=0, work=None,
+             nbytes=4096, out=None):
+    FAKE = ctypes.c_void_p(0x10000)
+    return lib.mx_predict_tensor_scale(FAKE if w is None else w, ldw, FAKE if g is None else g, ldg, src, rows,
+                                       cols, lr, fmt, FAKE if work is None else work, nbytes,
+                                       FAKE if out is None else out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=ctypes.c_void_p(0)), mx.MX_ERR_INVALID_ARG),
+    (dict(g=ctypes.c_void_p(0)), mx.MX_ERR_INVALID_ARG),
+    (dict(work=ctypes.c_void_p(0)), mx.MX_ERR_INVALID_ARG),
+    (dict(out=ctypes.c_void_p(0)), mx.MX_ERR_INVALID_ARG),
+    (dict(src=7), mx.MX_ERR_INVALID_ARG),
+    (dict(fmt=9), mx.MX_ERR_INVALID_ARG),
+    (dict(rows=0), mx.MX_ERR_INVALID_ARG),
+    (dict(ldw=32), mx.MX_ERR_INVALID_ARG),
+    (dict(ldg=63), mx.MX_ERR_INVALID_ARG),
+    (dict(lr=-1e-3), mx.MX_ERR_INVALID_ARG),
+    (dict(lr=float("nan")), mx.MX_ERR_INVALID_ARG),
+    (dict(lr=float("inf")), mx.MX_ERR_INVALID_ARG),
+    (dict(nbytes=4095), mx.MX_ERR_INVALID_ARG),
+    (dict(work=ctypes.c_void_p(0x10002)), mx.MX_ERR_ALIGNMENT),
+    (dict(out=ctypes.c_void_p(0x10001)), mx.MX_ERR_ALIGNMENT),
+    (dict(w=ctypes.c_void_p(0x10001)), mx.MX_ERR_ALIGNMENT),
+])
+def test_predict_tensor_scale_validation(lib, kw, status):
+    assert _predict(lib, **kw) == status
+    assert lib.mx_last_error_message().decode() != ""
+
+
+def test_predict_workspace_bytes(lib):
+    assert lib.mx_predict_workspace_bytes() == 4096
