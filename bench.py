@@ -137,6 +137,37 @@ def setup_dual(args):
     return step, info
 
 
+def setup_mxout(args):
+    """The MOSS two-level step with the GEMM writing its output already
+    MX-quantized (E4M3 codes [M][N] + E8M0 scales [M][N/32]) for the next
+    layer instead of bf16."""
+    step0, info = setup_moss(args)
+    w = info["host"]
+    A, B = to_dev(w["A"]), to_dev(w["B"])
+    M, K = A.shape
+    N = B.shape[1]
+    cfg = mx.qconfig("e4m3", two_level=True)
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N, K // 32), dtype=torch.uint8, device="cuda")
+    ta = torch.empty(1, dtype=torch.float32, device="cuda")
+    tb = torch.empty(1, dtype=torch.float32, device="cuda")
+    qc = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((M, N // 32), dtype=torch.uint8, device="cuda")
+
+    def step(t):
+        t.run("quant_A", lambda: mx.mx_quantize(A, mx.MX_AXIS_ROW, cfg, qa, sa, ta))
+        t.run("quant_B", lambda: mx.mx_quantize(B, mx.MX_AXIS_COL, cfg, qb, sb, tb))
+        t.run("gemm", lambda: mx.mx_gemm_quantized(qa, sa, ta, "e4m3", qb, sb, tb, "e4m3", M, N, K,
+                                                   out_fmt="e4m3", qc=qc, sc=sc))
+
+    info = dict(info)
+    info["config"] = dict(info["config"], workload="moss_two_level_e4m3_gemm_4096_mx_output",
+                          out="e4m3 codes + e8m0 1x32 scales")
+    return step, info
+
+
 def setup_autoscale(args):
     """MOSS weight auto-scaling: the next step's per-tensor scale predicted
     from this step's weight W and gradient G (one read of each), then the
@@ -266,7 +297,7 @@ def setup_copy(args):
 
 
 WORKLOADS = {"moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4, "llama": setup_llama,
-             "copy": setup_copy, "autoscale": setup_autoscale}
+             "copy": setup_copy, "autoscale": setup_autoscale, "mxout": setup_mxout}
 
 
 # ------------------------------------------------------------------ CPU baseline

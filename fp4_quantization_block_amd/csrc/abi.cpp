@@ -158,31 +158,75 @@ mx_status mx_predict_tensor_scale(const void* w, int64_t ld_w, const void* g, in
     return hip_status(mx::launch_predict(j, (hipStream_t)stream));
 }
 
+namespace {
+
+mx_status check_gemm_operands(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,
+                              const void* qb, const uint8_t* sb, const float* tb, int32_t fb,
+                              int64_t M, int64_t N, int64_t K, int32_t hadamard_k)
+{
+    if (!qa || !sa || !qb || !sb) return fail(MX_ERR_INVALID_ARG, "an operand pointer is NULL");
+    if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(MX_ERR_INVALID_ARG, "unknown element format");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(MX_ERR_INVALID_ARG, "M, N, K must be > 0");
+    if (K % 32 != 0) return fail(MX_ERR_INVALID_ARG, "K must be a multiple of 32");
+    if (hadamard_k != 0 && hadamard_k != 1) return fail(MX_ERR_INVALID_ARG, "hadamard_k must be 0 or 1");
+    if (elem_bits(fa) != elem_bits(fb)) return fail(MX_ERR_UNSUPPORTED, "mixed FP8 x FP4 operands are not built");
+    if (!aligned16(qa) || !aligned16(qb)) return fail(MX_ERR_ALIGNMENT, "qa and qb must be 16-byte aligned");
+    if (((reinterpret_cast<uintptr_t>(ta) | reinterpret_cast<uintptr_t>(tb)) & 3u) != 0)
+        return fail(MX_ERR_ALIGNMENT, "ta and tb must be 4-byte aligned");
+    return MX_OK;
+}
+
+mx::GemmJob gemm_job(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,
+                     const void* qb, const uint8_t* sb, const float* tb, int32_t fb,
+                     int64_t M, int64_t N, int64_t K, float alpha, int32_t hadamard_k)
+{
+    mx::GemmJob j{};
+    j.qa = (const uint8_t*)qa; j.sa = sa; j.ta = ta; j.fa = fa;
+    j.qb = (const uint8_t*)qb; j.sb = sb; j.tb = tb; j.fb = fb;
+    j.M = M; j.N = N; j.K = K;
+    j.alpha = alpha; j.hadamard_k = hadamard_k != 0;
+    return j;
+}
+
+}  // namespace
+
 mx_status mx_gemm(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,
                   const void* qb, const uint8_t* sb, const float* tb, int32_t fb,
                   int64_t M, int64_t N, int64_t K, float alpha, int32_t hadamard_k,
                   void* c, int32_t out_dtype, int64_t ldc, void* stream)
 {
     g_msg[0] = '\0';
-    if (!qa || !sa || !qb || !sb || !c) return fail(MX_ERR_INVALID_ARG, "an operand pointer is NULL");
-    if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(MX_ERR_INVALID_ARG, "unknown element format");
+    mx_status s = check_gemm_operands(qa, sa, ta, fa, qb, sb, tb, fb, M, N, K, hadamard_k);
+    if (s != MX_OK) return s;
+    if (!c) return fail(MX_ERR_INVALID_ARG, "an operand pointer is NULL");
     if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return fail(MX_ERR_INVALID_ARG, "unknown output dtype");
-    if (M <= 0 || N <= 0 || K <= 0) return fail(MX_ERR_INVALID_ARG, "M, N, K must be > 0");
-    if (K % 32 != 0) return fail(MX_ERR_INVALID_ARG, "K must be a multiple of 32");
     if (ldc < N) return fail(MX_ERR_INVALID_ARG, "ldc must be >= N");
-    if (hadamard_k != 0 && hadamard_k != 1) return fail(MX_ERR_INVALID_ARG, "hadamard_k must be 0 or 1");
-    if (elem_bits(fa) != elem_bits(fb)) return fail(MX_ERR_UNSUPPORTED, "mixed FP8 x FP4 operands are not built");
-    if (!aligned16(qa) || !aligned16(qb)) return fail(MX_ERR_ALIGNMENT, "qa and qb must be 16-byte aligned");
     const uintptr_t es = out_dtype == MX_OUT_F32 ? 4 : 2;
     if ((reinterpret_cast<uintptr_t>(c) % es) != 0) return fail(MX_ERR_ALIGNMENT, "c must be aligned to its element size");
-    if (((reinterpret_cast<uintptr_t>(ta) | reinterpret_cast<uintptr_t>(tb)) & 3u) != 0)
-        return fail(MX_ERR_ALIGNMENT, "ta and tb must be 4-byte aligned");
-    mx::GemmJob j{};
-    j.qa = (const uint8_t*)qa; j.sa = sa; j.ta = ta; j.fa = fa;
-    j.qb = (const uint8_t*)qb; j.sb = sb; j.tb = tb; j.fb = fb;
-    j.M = M; j.N = N; j.K = K;
-    j.alpha = alpha; j.hadamard_k = hadamard_k != 0;
+    mx::GemmJob j = gemm_job(qa, sa, ta, fa, qb, sb, tb, fb, M, N, K, alpha, hadamard_k);
     j.c = c; j.out_dtype = out_dtype; j.ldc = ldc;
+    return hip_status(mx::launch_gemm(j, (hipStream_t)stream));
+}
+
+mx_status mx_gemm_quantized(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,
+                            const void* qb, const uint8_t* sb, const float* tb, int32_t fb,
+                            int64_t M, int64_t N, int64_t K, float alpha, int32_t hadamard_k,
+                            int32_t out_fmt, void* qc, uint8_t* sc, void* stream)
+{
+    g_msg[0] = '\0';
+    mx_status s = check_gemm_operands(qa, sa, ta, fa, qb, sb, tb, fb, M, N, K, hadamard_k);
+    if (s != MX_OK) return s;
+    if (!qc || !sc) return fail(MX_ERR_INVALID_ARG, "qc and sc must not be NULL");
+    if (!valid_fmt(out_fmt)) return fail(MX_ERR_INVALID_ARG, "unknown output element format");
+    if (out_fmt == MX_E2M1) return fail(MX_ERR_UNSUPPORTED, "the quantized GEMM output is FP8 (E4M3 or E5M2)");
+    if (N % 32 != 0) return fail(MX_ERR_INVALID_ARG, "N must be a multiple of 32 (1x32 output blocks)");
+    if (!aligned16(qc)) return fail(MX_ERR_ALIGNMENT, "qc must be 16-byte aligned");
+    mx::GemmJob j = gemm_job(qa, sa, ta, fa, qb, sb, tb, fb, M, N, K, alpha, hadamard_k);
+    j.c = qc; j.cs = sc; j.ldc = N;
+    j.out_dtype = out_fmt == MX_E4M3 ? 2 : 3;
+    if (!mx::gemm_w4_eligible(j))
+        return fail(MX_ERR_UNSUPPORTED, "the quantized output needs rows of K holding a multiple of 128 bytes of "
+                                        "codes (FP8: K % 128 == 0, FP4: K % 256 == 0) and 4-byte aligned sa, sb");
     return hip_status(mx::launch_gemm(j, (hipStream_t)stream));
 }
 

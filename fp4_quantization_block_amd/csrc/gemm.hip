@@ -67,6 +67,7 @@ struct GArgs {
     int64_t M, N, K;
     float alpha; int hadamard_k;
     void* c; int64_t ldc;
+    uint8_t* cs;              // MX-quantized output: [M][N/32] scale bytes (c holds [M][N] codes)
     int tiles_m, tiles_n;
     int reg_path;             // 1: scale arrays not 4-byte aligned -> every stage via registers
 };
@@ -560,6 +561,30 @@ void k_gemm(GArgs g)
 // unit busy >90%, L1 waiting on pending L2 data half the time) at about 19
 // bytes per clock against the 32 a 256x256 FP8 tile needs at the MFMA
 // rate, with an average L2 latency near 370 cycles.
+// One 1x32 block of fp32 outputs to FP8 codes (FMT E4M3 / E5M2) and its
+// E8M0 scale byte, the same encoding as the quantizer's row copies with
+// round-to-nearest-even: shared exponent floor(log2 amax) - emax, exact
+// scaling, saturation, and a NaN block (0x7F codes, byte 0xFF) when the
+// block holds a NaN or Inf.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_out_block(const float (&v)[32], uint32_t* out)
+{
+    uint32_t key = 0;
+#pragma unroll
+    for (int k = 0; k < 32; k++) key = max(key, abs_key(v[k]));
+    if (key >= 0x7F800000u) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) out[k] = 0x7F7F7F7Fu;
+        return 0xFFu;
+    }
+    const int e = block_exponent<FMT>(key);
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        out[k] = cvt4_fp8<FMT>(clamp_fmax<FMT>(scale_by(v[4 * k], e)), clamp_fmax<FMT>(scale_by(v[4 * k + 1], e)),
+                               clamp_fmax<FMT>(scale_by(v[4 * k + 2], e)), clamp_fmax<FMT>(scale_by(v[4 * k + 3], e)));
+    return (uint32_t)(e + 127);
+}
+
 // k_gemm_w4's accumulators pinned to AGPRs (see pin above)
 __device__ __forceinline__ void pin4(f16v (&acc)[4][4])
 {
@@ -879,6 +904,48 @@ void k_gemm_w4(GArgs g)
                     if (gcol + k < g.N) dst[k] = e[k];
             }
         }
+    } else if constexpr (OUT >= 2) {
+        // MX-quantized output (OUT 2: E4M3, 3: E5M2), 1x32 blocks along the
+        // rows of C.  Each wave stages a 32-row slab of its quarter as fp32
+        // in its own LDS region (rows padded to 132 floats), then each lane
+        // encodes two of the slab's 128 row blocks and stores 32 code bytes
+        // and one scale byte per block.
+        constexpr int QF = OUT == 2 ? E4M3 : E5M2;
+        constexpr int PF = 132;
+        uint8_t* buf = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
+        float* ft = (float*)buf;
+        const int64_t nblk = g.N / 32;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    ft[(8 * (r / 4) + 4 * h + (r % 4)) * PF + j * 32 + l32] = acc[i][j][r] * ap;
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int b = lane + 64 * t, row = b >> 2, blk = b & 3;
+                float v[32];
+#pragma unroll
+                for (int m = 0; m < 8; m++) {
+                    const float4 x4 = *(const float4*)(ft + row * PF + blk * 32 + 4 * m);
+                    v[4 * m] = x4.x; v[4 * m + 1] = x4.y; v[4 * m + 2] = x4.z; v[4 * m + 3] = x4.w;
+                }
+                uint32_t codes[8];
+                const uint32_t sb = encode_out_block<QF>(v, codes);
+                const int64_t grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 128 + blk * 32;
+                if (grow < g.M && gcol < g.N) {
+                    uint8_t* dst = (uint8_t*)g.c + grow * g.N + gcol;
+                    *(uint4*)dst = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+                    *(uint4*)(dst + 16) = make_uint4(codes[4], codes[5], codes[6], codes[7]);
+                    g.cs[grow * nblk + gcol / 32] = (uint8_t)sb;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 4; i++)
@@ -904,17 +971,32 @@ hipError_t launch3(const GArgs& a, hipStream_t s)
         k_gemm_w4<FA, FB, OUT><<<dim3(nwg), dim3(256), 0, s>>>(a);
         return hipGetLastError();
     }
-    k_gemm<FA, FB, OUT><<<dim3(nwg), dim3(512), 0, s>>>(a);
-    return hipGetLastError();
+    if constexpr (OUT >= 2) {
+        return hipErrorInvalidValue;          // the MX-quantized output is built on k_gemm_w4 only
+    } else {
+        k_gemm<FA, FB, OUT><<<dim3(nwg), dim3(512), 0, s>>>(a);
+        return hipGetLastError();
+    }
 }
 
 template <int FA, int FB>
 hipError_t launch2(const GArgs& a, int out, hipStream_t s)
 {
-    return out == 0 ? launch3<FA, FB, 0>(a, s) : launch3<FA, FB, 1>(a, s);
+    switch (out) {
+    case 0: return launch3<FA, FB, 0>(a, s);
+    case 1: return launch3<FA, FB, 1>(a, s);
+    case 2: return launch3<FA, FB, 2>(a, s);
+    default: return launch3<FA, FB, 3>(a, s);
+    }
 }
 
 }  // namespace
+
+bool gemm_w4_eligible(const GemmJob& j)
+{
+    const int64_t kbytes = j.fa == E2M1 ? j.K / 2 : j.K;
+    return kbytes % BKB == 0 && (((uintptr_t)j.sa | (uintptr_t)j.sb) & 3u) == 0;
+}
 
 hipError_t launch_gemm(const GemmJob& j, hipStream_t stream)
 {
@@ -923,7 +1005,7 @@ hipError_t launch_gemm(const GemmJob& j, hipStream_t stream)
     a.qb = j.qb; a.sb = j.sb; a.tb = j.tb;
     a.M = j.M; a.N = j.N; a.K = j.K;
     a.alpha = j.alpha; a.hadamard_k = j.hadamard_k;
-    a.c = j.c; a.ldc = j.ldc;
+    a.c = j.c; a.ldc = j.ldc; a.cs = j.cs;
     a.tiles_m = (int)((j.M + BM - 1) / BM);
     a.tiles_n = (int)((j.N + BN - 1) / BN);
     a.reg_path = (((uintptr_t)j.sa | (uintptr_t)j.sb) & 3u) != 0;

@@ -49,9 +49,15 @@ struct GemmJob {
     const uint8_t* qb; const uint8_t* sb; const float* tb; int fb;
     int64_t M, N, K;
     float alpha; bool hadamard_k;
-    void* c; int out_dtype; int64_t ldc;
+    void* c; int out_dtype; int64_t ldc;   // out_dtype 0 f32, 1 bf16, 2 MX E4M3 codes, 3 MX E5M2 codes
+    uint8_t* cs;                            // MX output: [M][N/32] scale bytes
 };
 
 hipError_t launch_gemm(const GemmJob& j, hipStream_t stream);
+
+// whether launch_gemm takes the one-wave-per-SIMD kernel (the only one with
+// the MX-quantized output): rows of K holding a multiple of 128 bytes of
+// codes, 4-byte aligned scale arrays
+bool gemm_w4_eligible(const GemmJob& j);
 
 }  // namespace mx

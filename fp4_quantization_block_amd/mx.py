@@ -26,7 +26,7 @@ MX_OUT_F32, MX_OUT_BF16 = 0, 1
 FMTS = {"e4m3": MX_E4M3, "e5m2": MX_E5M2, "e2m1": MX_E2M1}
 EXPORTED = ("mx_quantize", "mx_quantize_dual_layout", "mx_gemm", "mx_dequantize",
             "mx_status_string", "mx_last_error_message",
-            "mx_predict_tensor_scale", "mx_predict_workspace_bytes")
+            "mx_predict_tensor_scale", "mx_predict_workspace_bytes", "mx_gemm_quantized")
 
 
 class MXError(RuntimeError):
@@ -67,6 +67,9 @@ def load() -> ctypes.CDLL:
                           ctypes.c_float, _i32, _vp, _i32, _i64, _vp]
     L.mx_dequantize.restype = _i32
     L.mx_dequantize.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i32, _i32, _vp, _i32, _vp]
+    L.mx_gemm_quantized.restype = _i32
+    L.mx_gemm_quantized.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64,
+                                    ctypes.c_float, _i32, _i32, _vp, _vp, _vp]
     L.mx_predict_tensor_scale.restype = _i32
     L.mx_predict_tensor_scale.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, ctypes.c_float, _i32,
                                           _vp, _i64, _vp, _vp]
@@ -186,6 +189,19 @@ def mx_gemm(qa, sa, ta, fa, qb, sb, tb, fb, M: int, N: int, K: int, alpha: float
                           _fmt(fb), M, N, K, float(alpha), int(bool(hadamard_k)), _ptr(c),
                           out_dtype, ldc, _stream(stream)))
     return c
+
+
+def mx_gemm_quantized(qa, sa, ta, fa, qb, sb, tb, fb, M: int, N: int, K: int, out_fmt="e4m3",
+                      alpha: float = 1.0, hadamard_k: bool = False, qc=None, sc=None, stream=None):
+    """GEMM with the output written as MX codes [M][N] and E8M0 scales [M][N/32]."""
+    if qc is None:
+        qc = torch.empty((M, N), dtype=torch.uint8, device=qa.device)
+    if sc is None:
+        sc = torch.empty((M, N // 32), dtype=torch.uint8, device=qa.device)
+    _check(load().mx_gemm_quantized(_ptr(qa), _ptr(sa), _ptr(ta), _fmt(fa), _ptr(qb), _ptr(sb), _ptr(tb),
+                                    _fmt(fb), M, N, K, float(alpha), int(bool(hadamard_k)), _fmt(out_fmt),
+                                    _ptr(qc), _ptr(sc), _stream(stream)))
+    return qc, sc
 
 
 def mx_predict_tensor_scale(w: torch.Tensor, g: torch.Tensor, lr: float, fmt,

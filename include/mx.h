@@ -165,6 +165,30 @@ mx_status mx_gemm(const void* qa, const uint8_t* sa, const float* ta, int32_t fa
                   void* c, int32_t out_dtype, int64_t ldc, void* stream);
 
 /*
+ * mx_gemm_quantized -- mx_gemm whose epilogue writes C already MX-quantized
+ * for the next layer ([FAF, "格式感知融合的设计思路"]: the producer emits
+ * the layout and format its consumer reads, with no separate pass over a
+ * bf16 C).  The fp32 value of each output is exactly the one mx_gemm
+ * writes with MX_OUT_F32 (alpha' * accumulator, one fp32 multiply); those
+ * values are then encoded as mx_quantize does for MX_AXIS_ROW with
+ * MX_SCALE_E8M0 and MX_RNE: 1x32 blocks along each row of C, shared
+ * exponent floor(log2 amax) - emax, saturating round-to-nearest-even.
+ *
+ * Operands, alpha, hadamard_k: as mx_gemm.
+ * out_fmt: MX_E4M3 or MX_E5M2 (E2M1: MX_ERR_UNSUPPORTED).
+ * qc:    [M][N] codes, dense (row stride N bytes), 16-byte aligned.
+ * sc:    [M][N/32] E8M0 scale bytes.
+ * Needs N % 32 == 0, and the operands in the form the fast GEMM kernel
+ * takes: rows of K holding a multiple of 128 bytes of codes (FP8: K % 128
+ * == 0; FP4: K % 256 == 0) and 4-byte aligned sa, sb (else
+ * MX_ERR_UNSUPPORTED).  Other errors as mx_gemm.
+ */
+mx_status mx_gemm_quantized(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,
+                            const void* qb, const uint8_t* sb, const float* tb, int32_t fb,
+                            int64_t M, int64_t N, int64_t K, float alpha, int32_t hadamard_k,
+                            int32_t out_fmt, void* qc, uint8_t* sc, void* stream);
+
+/*
  * mx_dequantize -- inverse of mx_quantize ([MOSS, "两级缩放实现"]:
  * micro-scale first, then the tensor scale): per element
  * decode(code) * 2^(byte-127) (exact in fp32), then, if `hadamard`, the

@@ -159,3 +159,27 @@ def test_predict_tensor_scale_validation(lib, kw, status):
 
 def test_predict_workspace_bytes(lib):
     assert lib.mx_predict_workspace_bytes() == 4096
+
+
+def _gemmq(lib, M=64, N=64, K=128, fa=0, fb=0, out_fmt=0, qc=None, sc=None, sa=None):
+    FAKE = ctypes.c_void_p(0x10000)
+    return lib.mx_gemm_quantized(FAKE, FAKE if sa is None else sa, None, fa, FAKE, FAKE, None, fb, M, N, K, 1.0, 0,
+                                 out_fmt, FAKE if qc is None else qc, FAKE if sc is None else sc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qc=ctypes.c_void_p(0)), mx.MX_ERR_INVALID_ARG),
+    (dict(sc=ctypes.c_void_p(0)), mx.MX_ERR_INVALID_ARG),
+    (dict(out_fmt=7), mx.MX_ERR_INVALID_ARG),
+    (dict(out_fmt=2), mx.MX_ERR_UNSUPPORTED),          # E2M1 output
+    (dict(N=48), mx.MX_ERR_INVALID_ARG),               # N % 32
+    (dict(qc=ctypes.c_void_p(0x10008)), mx.MX_ERR_ALIGNMENT),
+    (dict(K=96), mx.MX_ERR_UNSUPPORTED),               # FP8 needs K % 128
+    (dict(fa=2, fb=2, K=128), mx.MX_ERR_UNSUPPORTED),  # FP4 needs K % 256
+    (dict(sa=ctypes.c_void_p(0x10002)), mx.MX_ERR_UNSUPPORTED),
+    (dict(fa=0, fb=2), mx.MX_ERR_UNSUPPORTED),         # mixed FP8 x FP4
+    (dict(K=100), mx.MX_ERR_INVALID_ARG),
+])
+def test_gemm_quantized_validation(lib, kw, status):
+    assert _gemmq(lib, **kw) == status
+    assert lib.mx_last_error_message().decode() != ""
