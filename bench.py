@@ -52,6 +52,9 @@ MEASURED_TRAFFIC = {
     # the fused amax pass of the prediction (k_amax_partial2)
     "autoscale": {"source": "quant.hip", "sha256": "34af4648077c908f",
                   "fetch_kib": 32812.4, "write_kib": 32.0},
+    # the dual-layout quantizer (k_quant_tile_dma)
+    "dual": {"source": "quant.hip", "sha256": "34af4648077c908f",
+             "fetch_kib": 229528.2, "write_kib": 496866.7},
 }
 
 
