@@ -8,9 +8,18 @@
 //
 // Sources:
 //   [MOSS] "MOSS: 用微缩放和自动缩放实现无损 FP8 训练，OLMo-7B 加速 34%"
+//   [FAF]  "格式感知融合:让FP4预训练提速两倍的工程实践"
 //
 // C[M][N] = alpha' * A[M][K] . B[N][K]^T, A/B as written by the quantizer
-// (K contiguous codes, [rows][K/32] E8M0 scales).
+// (K contiguous codes, [rows][K/32] E8M0 scales).  The output is fp32,
+// bf16, or -- [FAF, "格式感知融合的设计思路"], the producer writing its
+// consumer's format -- FP8 codes with E8M0 1x32 row scales.
+//
+// Two kernels.  k_gemm_w4 (one wave per SIMD, described at its definition)
+// runs every GEMM whose rows of K hold a multiple of 128 bytes of codes and
+// whose scale arrays are 4-byte aligned, and is the only one with the
+// MX-quantized output.  k_gemm below takes the rest (a ragged last K stage,
+// unaligned scale arrays):
 //
 // Tiling: 256x256 output tile per 512-thread workgroup (2x4 waves, 128x64
 // per wave = 4x2 MFMA 32x32 tiles, fp32 accumulators in AGPRs).  Two waves
@@ -532,35 +541,34 @@ void k_gemm(GArgs g)
 }
 
 // ---------------------------------------------------------------------------
-// k_gemm_w4: FP8 x FP8 with K a multiple of 128 and 4-byte aligned scale
-// arrays.  One wave per SIMD: a 256-thread workgroup computes the same
-// 256x256 tile, each wave a 128x128 quarter (4x4 MFMA 32x32 tiles, all 256
-// accumulator registers).  Compared with two 128x64 waves per SIMD this
-// reads a third less from LDS per MFMA (8 fragments per 16 MFMAs instead of
-// 6 per 8), and lets each wave overlap its own loads with its MFMAs instead
-// of trading phases with a partner wave at barriers.
+// k_gemm_w4: rows of K holding a multiple of 128 bytes of codes (FP8: K %
+// 128 == 0, FP4: K % 256 == 0) and 4-byte aligned scale arrays.  One wave
+// per SIMD: a 256-thread workgroup computes a 256x256 tile, each wave a
+// 128x128 quarter (4x4 MFMA 32x32 tiles, all 256 accumulator registers).
+// Compared with two 128x64 waves per SIMD this reads a third less from LDS
+// per MFMA (8 fragments per 16 MFMAs instead of 6 per 8), and lets each
+// wave overlap its own loads with its MFMAs instead of trading phases with
+// a partner wave at barriers.
 //
 // Operand tiles travel global -> registers -> LDS: each thread holds one
 // stage's share (16 chunks of 16 bytes, 64 VGPRs) between its global load
-// and its LDS write, which gives every load a whole stage to arrive.  Per
-// stage (128 bytes of K per row, two MFMA k-steps) each wave runs:
-//   phase A: the 16 MFMAs of k-step 0, each followed by one slot of other
-//            work: the LDS reads of k-step 1's fragments, and the LDS write
-//            and reload of part of a later stage;
-//   barrier (this wave's LDS reads and writes complete);
-//   phase B: the 16 MFMAs of k-step 1, each followed by the LDS reads of the
-//            next stage's k-step 0 fragments and the rest of the writes.
-// LDS holds two stage buffers (2 x 64 KiB plus scales); the schedule of the
-// writes into them is given at the main loop.  Rows past M (N) read as zero
-// and their outputs are dropped; loads of stages past the end re-read the
-// last stage into buffers nothing reads any more.
+// and its LDS write, which gives every load a whole stage to arrive.  A
+// stage is 128 bytes of K per row: two MFMA k-steps for FP8, four for FP4.
+// Each k-step is a phase of 16 MFMAs, each followed by one slot of other
+// work: the LDS reads of the next k-step's fragments (the two fragment
+// sets alternate), and the LDS writes and reloads of later stages.  One
+// barrier per stage, before the last phase, which reads the next stage.
+// LDS holds two stage buffers (2 x 64 KiB plus scales); the schedule of
+// the writes into them is given at the main loop.  Rows past M (N) read as
+// zero and their outputs are dropped; loads of stages past the end re-read
+// the last stage into buffers nothing reads any more.
 //
 // Measured bound: with the loads taken out of the loop the same schedule
 // runs the MFMAs at 77% of the FP8 peak at long K, so the loads set the
 // pace.  Counters show each CU's vector-memory path saturated (address
-// unit busy >90%, L1 waiting on pending L2 data half the time) at about 19
-// bytes per clock against the 32 a 256x256 FP8 tile needs at the MFMA
-// rate, with an average L2 latency near 370 cycles.
+// unit busy 65-93%, L1 waiting on pending L2 data 30-50% of cycles) at
+// about 19 bytes per clock against the 32 a 256x256 FP8 tile needs at the
+// MFMA rate, with an average L2 latency of 270-370 cycles.
 // One 1x32 block of fp32 outputs to FP8 codes (FMT E4M3 / E5M2) and its
 // E8M0 scale byte, the same encoding as the quantizer's row copies with
 // round-to-nearest-even: shared exponent floor(log2 amax) - emax, exact
