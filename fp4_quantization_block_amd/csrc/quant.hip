@@ -449,14 +449,21 @@ __device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt vmcnt(0)
 // ---------------------------------------------------------------------------
 template <int SRC> struct DmaTile {
     static constexpr int EB = SrcT<SRC>::bytes, ROWS = 128, COLS = 256 / EB, RB = 256;
-    // rows padded by 16 bytes: 16 consecutive rows read with ds_read_b128
-    // start in 16 different bank groups; a row read by consecutive lanes is
-    // contiguous
-    static constexpr int PITCH = RB + 16, BYTES = ROWS * PITCH;
+    // dense 256-byte rows whose 16-byte chunks are XOR-permuted by the row
+    // (chunk c of row r sits at position c ^ (r & 15)): 16 consecutive rows
+    // read with ds_read_b128 at one chunk hit 16 different bank groups, a
+    // row read by consecutive lanes stays inside its row, and four rows
+    // form one contiguous 1 KiB run, the unit of a 16-byte-per-lane direct
+    // load
+    static constexpr int BYTES = ROWS * RB;
     // compute waves: one column block and one row block per thread for bf16
     static constexpr int NCW = SRC == SRC_BF16 ? 8 : 4;
-    __device__ static int at(int row, int byte) { return row * PITCH + byte; }
+    __device__ static int at(int row, int byte) { return row * RB + ((((byte >> 4) ^ (row & 15))) << 4) + (byte & 15); }
 };
+
+// loader wait at the end of a tile when the tile after next is in flight:
+// all but its 32 direct loads (the next tile's) complete, then the barrier
+__device__ __forceinline__ void dma_barrier_keep32() { asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory"); }
 
 // Output staging of LB-byte lines (LB = 32, 64 or 128): the 16-byte chunks of
 // a line are XOR-permuted so that 16 lanes writing one chunk of 16
@@ -492,47 +499,57 @@ __global__ __launch_bounds__(64 * (DmaTile<SRC>::NCW + 1)) void k_quant_tile_dma
     constexpr int SPR = TCC / 32;               // row scale bytes per tile row
     static_assert(NT >= 1 && TRR * TCC / 32 == NT * NCT, "tile / thread split");
     static_assert(TCC * LBC + TRR * LBR <= T::BYTES, "staging fits the tile buffer");
+    // three tile buffers: tile k is read while k+1 lands and k+2 is loading
     __shared__ __align__(16) uint8_t buf0[T::BYTES];
     __shared__ __align__(16) uint8_t buf1[T::BYTES];
+    __shared__ __align__(16) uint8_t buf2[T::BYTES];
     __shared__ __align__(4) uint8_t sc_col[TCC * 4];
     __shared__ __align__(4) uint8_t sc_row[TRR * SPR];
 
     const int tid = threadIdx.x;
     if (tid >= NCT) {
         // ---------------- loader wave ----------------
-        const uint32_t voff = (uint32_t)(4 * (tid - NCT));
+        // 32 direct loads per tile, 16 bytes per lane: load p fills the
+        // contiguous 1 KiB of tile rows 4p .. 4p+3; lane l writes LDS chunk
+        // position l % 16 of row 4p + l / 16, i.e. source chunk
+        // (l % 16) ^ (row & 15).  The row offset is part of the range-checked
+        // lane offset, so rows past the tensor (and, with cols * elem a
+        // multiple of 16, bytes past its end) read as zero.
+        const int l = tid - NCT;
+        const uint32_t lrow = (uint32_t)(l >> 4), lcp = (uint32_t)(l & 15);
         auto issue = [&](int64_t r0, int64_t c0, uint8_t* dst) {
             int64_t n = ((a.rows - r0 - 1) * a.ld + (a.cols - c0)) * EB;
             n = n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n;
             const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)((const uint8_t*)a.x + (r0 * a.ld + c0) * EB), (short)0, (int)(uint32_t)n, 0x00020000);
             const uint32_t row_bytes = (uint32_t)(a.ld * EB);
-            // The buffer range check covers the lane offset, not soffset.  A
-            // tile whose 128 rows lie inside the tensor, and whose last row's
-            // 256 bytes do not run past the tensor's end, keeps the row
-            // offset in soffset; an edge tile loads only its rows inside the
-            // tensor, with the row offset in the checked lane offset.
-            if (a.rows - r0 >= TRR && (a.rows - r0 > TRR || a.cols - c0 >= TCC)) {
 #pragma unroll 8
-                for (int j = 0; j < TRR; j++)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + j * T::PITCH), 4, voff,
-                                                             j * row_bytes, 0, 0);
-            } else {
-                const int nv = (int)(a.rows - r0 < TRR ? a.rows - r0 : TRR);
-                for (int j = 0; j < nv; j++)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + j * T::PITCH), 4,
-                                                             voff + j * row_bytes, 0, 0, 0);
+            for (int p = 0; p < TRR / 4; p++) {
+                const uint32_t row = 4 * p + lrow;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + p * 1024), 16,
+                                                         row * row_bytes + ((lcp ^ (row & 15)) << 4), 0, 0, 0);
             }
         };
-        int64_t r0, c0;
+        int64_t r0, c0, r1, c1;
         if (tile_at<TRR, TCC>(a, 0, r0, c0)) issue(r0, c0, buf0);
-        dma_barrier();
+        if (tile_at<TRR, TCC>(a, 1, r1, c1)) {
+            issue(r1, c1, buf1);
+            dma_barrier_keep32();                          // tile 0 landed
+        } else {
+            dma_barrier();
+        }
         for (int64_t k = 0; tile_at<TRR, TCC>(a, k, r0, c0); k++) {
-            int64_t r1, c1;
-            if (tile_at<TRR, TCC>(a, k + 1, r1, c1)) issue(r1, c1, (k & 1) ? buf0 : buf1);
+            // tile k+2 goes to the buffer of tile k-1, free since the end of k-1
+            int64_t r2, c2;
+            const bool next2 = tile_at<TRR, TCC>(a, k + 2, r2, c2);
+            if (next2) {
+                const int m = (int)((k + 2) % 3);
+                issue(r2, c2, m == 0 ? buf0 : m == 1 ? buf1 : buf2);
+            }
             lds_barrier();                                // compute: tile read
             lds_barrier();                                // compute: codes staged
-            dma_barrier();                                // end of tile
+            if (next2) dma_barrier_keep32();              // end of tile: tile k+1 landed
+            else dma_barrier();
         }
         return;
     }
@@ -542,7 +559,8 @@ __global__ __launch_bounds__(64 * (DmaTile<SRC>::NCW + 1)) void k_quant_tile_dma
     lds_barrier();
     int64_t r0, c0;
     for (int64_t k = 0; tile_at<TRR, TCC>(a, k, r0, c0); k++) {
-        uint8_t* tile = (k & 1) ? buf1 : buf0;
+        const int km = (int)(k % 3);
+        uint8_t* tile = km == 0 ? buf0 : km == 1 ? buf1 : buf2;
         int nrow, ncol;
         tile_extent<TRR, TCC>(a, r0, c0, nrow, ncol);
         uint32_t ccode[NT][CW], csc[NT], rcode[NT][CW], rsc[NT];
@@ -860,6 +878,7 @@ hipError_t launch_tile(QArgs a, hipStream_t stream)
     // 4096^2 to 16384x14336 (the per-element division weighs more than the
     // loads), while plain column copies are 4-6% faster with direct loads.
     const bool dma = !SR && !(!ROW && a.two_level) && a.vec != 0 &&
+                     (a.cols * SrcT<SRC>::bytes) % 16 == 0 &&
                      a.ld * SrcT<SRC>::bytes * 128 < (int64_t(1) << 32);
     const size_t dyn = SR ? (size_t)TR * TC * sizeof(uint32_t) : 0;
     const int tcols = dma ? DmaTile<SRC>::COLS : TC, trows = dma ? DmaTile<SRC>::ROWS : TR;
