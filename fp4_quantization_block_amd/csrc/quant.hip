@@ -926,8 +926,10 @@ hipError_t launch_fmt(const QuantJob& j, hipStream_t stream)
         const int64_t cap = (sbytes - (int64_t)pad) / 4;
         const int flat16 = a.vec && j.ld == j.cols;
         const int64_t nwords = j.rows * j.cols * es / 16;
-        int64_t want = flat16 ? (nwords + 2047) / 2048 : j.rows;
-        want = want < 1 ? 1 : (want > 512 ? 512 : want);
+        // at most 256 partials (one workgroup per CU): measured 0-3.5% faster
+        // than 128 or 512-4096 at 4096^2 to 16384x14336
+        int64_t want = flat16 ? (nwords + 4095) / 4096 : j.rows;
+        want = want < 1 ? 1 : (want > 256 ? 256 : want);
         uint32_t* partial = (uint32_t*)(sbuf + pad);
         int64_t n = want < cap ? want : cap;
         if (n < 1) {                       // tiny tensor: the tensor-scale word holds the key
