@@ -18,17 +18,18 @@
 //                 from global memory (64 contiguous bytes per lane for bf16),
 //                 no cross-lane traffic.
 //   k_quant_tile_dma / k_quant_tile_reg   column copy, or both copies from
-//                 one read.  Persistent workgroups walk 128-row x 64-column
-//                 tiles held raw in LDS; each of 256 compute threads then
-//                 quantizes one 1x32 row block and one 32x1 column block.
-//                 Column copies are stored transposed, a 128-byte run per
-//                 column and tile.  The _dma form (16-byte-aligned sources)
-//                 adds a loader wave that streams the next tile straight into
-//                 a second LDS buffer while the current one is quantized; the
-//                 _reg form prefetches into registers and handles any
-//                 alignment.  For stochastic rounding of column blocks the
-//                 workgroup generates the tile's Philox words into LDS, four
-//                 per call, so no word is wasted.
+//                 one read.  Persistent workgroups walk tiles held raw in
+//                 LDS; each compute thread quantizes row and column blocks
+//                 of the tile.  Column copies are stored transposed, a
+//                 128-byte (FP8) run per column and tile.  The _dma form
+//                 (round to nearest, 16-byte-aligned sources; tiles of 128
+//                 rows x 256 source bytes) adds a loader wave that streams
+//                 tiles two ahead into three LDS buffers with direct loads;
+//                 the _reg form (stochastic rounding, or any alignment;
+//                 128 x 64 tiles) prefetches the next tile into registers.
+//                 For stochastic rounding of column blocks the workgroup
+//                 generates the tile's Philox words into LDS, four per
+//                 call, so no word is wasted.
 //   k_amax_partial / k_amax_reduce   level-1 tensor amax for the two-level
 //                 scheme: per-workgroup partial maxima, then one workgroup
 //                 writes s_t = amax / Fmax.  The partials are parked in the
@@ -434,17 +435,20 @@ __device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt vmcnt(0)
 // ---------------------------------------------------------------------------
 // k_quant_tile_dma: 16-byte-aligned sources, round to nearest.  Tiles of
 // 128 rows x 256 source bytes (128 bf16 or 64 fp32 columns).  NCW compute
-// waves plus one loader wave: the loader streams the next tile straight into
-// the other LDS buffer (direct global->LDS buffer loads, one 256-byte tile row
-// per instruction; rows past the tensor are skipped, columns past it hold
-// neighbouring data or zeros, and neither is used) while the compute waves
-// quantize the current one, so the compute waves never wait on a global load
-// and the loader never waits on a store.  Codes are staged back into the tile's own
-// LDS buffer once every block has been read, then written out as whole runs:
+// waves plus one loader wave: the loader streams tiles two ahead into three
+// LDS tile buffers (direct global->LDS buffer loads of 16 bytes per lane;
+// rows past the tensor read as zero, columns past it hold neighbouring data
+// or zeros, and neither is used) while the compute waves quantize the
+// current one, so the compute waves never wait on a global load and the
+// loader never waits on a store.  Codes are staged in an LDS buffer of their
+// own, then written out as whole runs:
 // each column's codes for the tile form one 128-byte (FP8) or 64-byte (FP4)
 // run of the transposed copy, each row's one run of the row copy, and scale
-// bytes leave four to a store.  Scattered 16- to 32-byte stores (one per
-// block) were measured at under 2.2 TB/s on this part; whole runs reach the
+// bytes leave four to a store.  Two barriers per tile: one when every block
+// of the tile has been read (its buffer is then free for the loader), one
+// when the codes are staged and the next tile has landed.  Scattered 16- to
+// 32-byte stores (one per block) were measured at under 2.2 TB/s on this
+// part; whole runs reach the
 // HBM rate.
 // ---------------------------------------------------------------------------
 template <int SRC> struct DmaTile {
@@ -498,11 +502,13 @@ __global__ __launch_bounds__(64 * (DmaTile<SRC>::NCW + 1)) void k_quant_tile_dma
     constexpr int NT = TRR * TCC / 32 / NCT;    // column (and row) blocks per compute thread
     constexpr int SPR = TCC / 32;               // row scale bytes per tile row
     static_assert(NT >= 1 && TRR * TCC / 32 == NT * NCT, "tile / thread split");
-    static_assert(TCC * LBC + TRR * LBR <= T::BYTES, "staging fits the tile buffer");
-    // three tile buffers: tile k is read while k+1 lands and k+2 is loading
+    // three tile buffers: tile k is read while k+1 lands and k+2 is loading;
+    // the codes are staged in a buffer of their own, so a tile buffer is free
+    // for the loader as soon as its blocks have been read
     __shared__ __align__(16) uint8_t buf0[T::BYTES];
     __shared__ __align__(16) uint8_t buf1[T::BYTES];
     __shared__ __align__(16) uint8_t buf2[T::BYTES];
+    __shared__ __align__(16) uint8_t stg[TCC * LBC + TRR * LBR];
     __shared__ __align__(4) uint8_t sc_col[TCC * 4];
     __shared__ __align__(4) uint8_t sc_row[TRR * SPR];
 
@@ -539,16 +545,16 @@ __global__ __launch_bounds__(64 * (DmaTile<SRC>::NCW + 1)) void k_quant_tile_dma
             dma_barrier();
         }
         for (int64_t k = 0; tile_at<TRR, TCC>(a, k, r0, c0); k++) {
-            // tile k+2 goes to the buffer of tile k-1, free since the end of k-1
+            // tile k+2 goes to the buffer of tile k-1, free since every block
+            // of tile k-1 was read
             int64_t r2, c2;
             const bool next2 = tile_at<TRR, TCC>(a, k + 2, r2, c2);
             if (next2) {
                 const int m = (int)((k + 2) % 3);
                 issue(r2, c2, m == 0 ? buf0 : m == 1 ? buf1 : buf2);
             }
-            lds_barrier();                                // compute: tile read
-            lds_barrier();                                // compute: codes staged
-            if (next2) dma_barrier_keep32();              // end of tile: tile k+1 landed
+            lds_barrier();                                // compute: tile k read
+            if (next2) dma_barrier_keep32();              // codes staged; tile k+1 landed
             else dma_barrier();
         }
         return;
@@ -606,11 +612,13 @@ __global__ __launch_bounds__(64 * (DmaTile<SRC>::NCW + 1)) void k_quant_tile_dma
                 }
             }
         }
-        lds_barrier();                                   // every block of the tile has been read
+        // every block of the tile has been read, and every wave's reads of
+        // the previous tile's staged codes have completed
+        lds_barrier();
 
         // stage codes and scales (column runs first, then row runs)
-        uint8_t* scol = tile;
-        uint8_t* srow = tile + TCC * LBC;
+        uint8_t* scol = stg;
+        uint8_t* srow = stg + TCC * LBC;
 #pragma unroll
         for (int j = 0; j < NT; j++) {
             const int q = tid + NCT * j, c = q % TCC, rb = q / TCC;
@@ -635,9 +643,10 @@ __global__ __launch_bounds__(64 * (DmaTile<SRC>::NCW + 1)) void k_quant_tile_dma
                 }
             }
         }
-        lds_barrier();                                   // staging complete
+        lds_barrier();                                   // staging complete; tile k+1 landed
 
-        // whole runs out
+        // whole runs out (the next tile's reads of its own buffer follow
+        // without a barrier)
         const int64_t colbytes = a.rows * BITS / 8, rowbytes = a.cols * BITS / 8;
         for (int id = tid; id < TCC * (LBC / 16); id += NCT) {
             const int line = id / (LBC / 16), ch = id % (LBC / 16);
@@ -664,7 +673,6 @@ __global__ __launch_bounds__(64 * (DmaTile<SRC>::NCW + 1)) void k_quant_tile_dma
                 store_scales(a.s_row + (r0 + r) * (a.cols / 32) + c0 / 32, w, ncol / 32);
             }
         }
-        lds_barrier();                                   // tile buffer free for the loader
     }
 }
 
@@ -874,10 +882,9 @@ hipError_t launch_tile(QArgs a, hipStream_t stream)
     // direct loads address a tile's rows with 32-bit offsets from its first
     // row; stochastic rounding (bound by its Philox arithmetic) stays on the
     // register-fed kernel, whose tile also holds the column words.  Column
-    // copies with a tensor scale go there too: measured 4-15% faster at
-    // 4096^2 to 16384x14336 (the per-element division weighs more than the
-    // loads), while plain column copies are 4-6% faster with direct loads.
-    const bool dma = !SR && !(!ROW && a.two_level) && a.vec != 0 &&
+    // copies with a tensor scale take the direct-load kernel too: measured
+    // 17% faster at 16384x14336, within 1% either way at 4096^2 to 8192^2.
+    const bool dma = !SR && a.vec != 0 &&
                      (a.cols * SrcT<SRC>::bytes) % 16 == 0 &&
                      a.ld * SrcT<SRC>::bytes * 128 < (int64_t(1) << 32);
     const size_t dyn = SR ? (size_t)TR * TC * sizeof(uint32_t) : 0;
