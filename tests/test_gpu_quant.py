@@ -64,7 +64,7 @@ def run_gpu(xd, mode, fmt, opts):
         qr, sr_, qc, sc, ts = mx.mx_quantize_dual_layout(xd, cfg)
         torch.cuda.synchronize()
         return (u8(qr), u8(sr_)), (u8(qc), u8(sc)), ts
-    axis = mx.MX_AXIS_ROW if mode == "row" else mx.MX_AXIS_COL
+    axis = mx.MX_AXIS_ROW if mode == "row" else mx.MX_AXIS_COL      # "col", "col16": column copy
     q, s, ts = mx.mx_quantize(xd, axis, cfg)
     torch.cuda.synchronize()
     out = (u8(q), u8(s))
@@ -78,11 +78,14 @@ def run_oracle(x, axis, fmt, opts):
     return q, s, st
 
 
-SHAPES = {"row": (45, 160), "col": (96, 37), "dual": (160, 288)}
+# "col" rows are not 16-byte multiples (register-fed kernel); "col16" rows are,
+# so its round-to-nearest cases run on the direct-load kernel, with a partial
+# last tile in both directions
+SHAPES = {"row": (45, 160), "col": (96, 37), "col16": (160, 200), "dual": (160, 288)}
 
 
 @pytest.mark.parametrize("opt", list(OPTIONS))
-@pytest.mark.parametrize("mode", ["row", "col", "dual"])
+@pytest.mark.parametrize("mode", ["row", "col", "col16", "dual"])
 @pytest.mark.parametrize("src", ["f32", "bf16"])
 @pytest.mark.parametrize("fmt", FMTS)
 def test_quantize_small_all_options(fmt, src, mode, opt):
@@ -154,6 +157,21 @@ def test_provided_tensor_scale():
     assert_codes_equal(u8(q), qo, "codes")
     assert_codes_equal(u8(s), so, "scales")
     assert ts.item() == st                # provided scale is read, not written
+
+
+def test_provided_tensor_scale_column_copy():
+    """Provided s_t on a column copy whose rows are 16-byte multiples (the
+    direct-load kernel), ragged in both directions."""
+    rng = np.random.default_rng(5)
+    x = I.to_bf16_bits(rng.standard_normal((160, 200)).astype(np.float32) * 30)
+    st = np.float32(0.0371)
+    ts = torch.tensor([st], dtype=torch.float32, device=DEV)
+    cfg = mx.qconfig("e4m3", two_level=True, tscale_provided=True)
+    q, s, _ = mx.mx_quantize(to_device(x), mx.MX_AXIS_COL, cfg, tensor_scale=ts)
+    qo, so, _ = O.quantize(x, O.AXIS_COL, "e4m3", two_level=2, tensor_scale=float(st))
+    assert_codes_equal(u8(q), qo, "codes")
+    assert_codes_equal(u8(s), so, "scales")
+    assert ts.item() == st
 
 
 def test_strided_source():
