@@ -185,6 +185,21 @@ def test_strided_source():
     assert_codes_equal(u8(s), so, "scales")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_strided_source_two_level_column_copy(fmt):
+    """ld > cols with a computed tensor scale, column copy: the amax pass walks
+    rows, and the direct-load kernel addresses rows by ld (row bytes are
+    16-byte multiples); a partial last tile in both directions."""
+    rng = np.random.default_rng(6)
+    full = I.to_bf16_bits(rng.standard_normal((160, 232)).astype(np.float32) * 7)
+    xd = to_device(full)[:, :200]
+    q, s, ts = mx.mx_quantize(xd, mx.MX_AXIS_COL, mx.qconfig(fmt, two_level=True))
+    qo, so, st = O.quantize(np.ascontiguousarray(full[:, :200]), O.AXIS_COL, fmt, two_level=1)
+    assert_codes_equal(u8(q), qo, "codes")
+    assert_codes_equal(u8(s), so, "scales")
+    assert_same_f32(ts.cpu().numpy(), [st])
+
+
 def test_deterministic_repeat():
     rng = np.random.default_rng(5)
     x = to_device(edge_rich(rng, 256, 512, "bf16"))
