@@ -40,15 +40,15 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0}   # dense scaled MFMA
 # commands are in profiles/.  Keyed by the SHA-256 of the kernel's source
 # file at measurement time: a changed kernel reports null until re-measured.
 MEASURED_TRAFFIC = {
-    "moss": {"source": "gemm.hip", "sha256": "bca8715ebfde6023",
-             "fetch_kib": 50811.5, "write_kib": 32768.0},
+    "moss": {"source": "gemm.hip", "sha256": "4e5111340904f308",
+             "fetch_kib": 50805.1, "write_kib": 32786.2},
     # the six GEMMs of one step together (the roofline's unit for this workload)
-    "llama": {"source": "gemm.hip", "sha256": "bca8715ebfde6023",
-              "fetch_kib": 3244562.4, "write_kib": 1163264.0},
-    "fp4": {"source": "gemm.hip", "sha256": "bca8715ebfde6023",
-            "fetch_kib": 183873.5, "write_kib": 49152.0},
-    "mxout": {"source": "gemm.hip", "sha256": "bca8715ebfde6023",
-              "fetch_kib": 50867.9, "write_kib": 16896.0},
+    "llama": {"source": "gemm.hip", "sha256": "4e5111340904f308",
+              "fetch_kib": 3235235.0, "write_kib": 1163977.8},
+    "fp4": {"source": "gemm.hip", "sha256": "4e5111340904f308",
+            "fetch_kib": 183584.7, "write_kib": 49154.8},
+    "mxout": {"source": "gemm.hip", "sha256": "4e5111340904f308",
+              "fetch_kib": 50868.1, "write_kib": 18782.1},
     # the fused amax pass of the prediction (k_amax_partial2)
     "autoscale": {"source": "quant.hip", "sha256": "44988e745806c8be",
                   "fetch_kib": 32811.5, "write_kib": 32.0},

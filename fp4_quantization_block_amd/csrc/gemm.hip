@@ -610,6 +610,17 @@ struct W4Frag {
     uint32_t sa[4], sb[4];
 };
 
+// Non-temporal stores for k_gemm_w4's output: nothing in the kernel reads C
+// back, and streaming it past L2 measured 7-8% faster for the whole GEMM at
+// 4096^3 and 8192x28672x4096 (the stores come in one burst at the end of
+// every tile, with the matrix cores idle).  Single scale bytes stay cached:
+// stored non-temporally they raised the bytes written by 30%.
+__device__ __forceinline__ void store_nt16(void* p, uint4 v)
+{
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, (u32x4v*)p);
+}
+
 template <int FA, int FB, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_w4(GArgs g)
@@ -905,7 +916,7 @@ void k_gemm_w4(GArgs g)
             const uint4 v = *(const uint4*)(ct + row * 128 + c8);
             uint16_t* dst = (uint16_t*)g.c + grow * g.ldc + gcol;
             if (vec && gcol + 8 <= g.N) {
-                *(uint4*)dst = v;
+                store_nt16(dst, v);
             } else {
                 const uint16_t* e = (const uint16_t*)&v;
                 for (int k = 0; k < 8; k++)
@@ -946,9 +957,9 @@ void k_gemm_w4(GArgs g)
                 const int64_t grow = m0 + wm * 128 + i * 32 + row, gcol = n0 + wn * 128 + blk * 32;
                 if (grow < g.M && gcol < g.N) {
                     uint8_t* dst = (uint8_t*)g.c + grow * g.N + gcol;
-                    *(uint4*)dst = make_uint4(codes[0], codes[1], codes[2], codes[3]);
-                    *(uint4*)(dst + 16) = make_uint4(codes[4], codes[5], codes[6], codes[7]);
-                    g.cs[grow * nblk + gcol / 32] = (uint8_t)sb;
+                    store_nt16(dst, make_uint4(codes[0], codes[1], codes[2], codes[3]));
+                    store_nt16(dst + 16, make_uint4(codes[4], codes[5], codes[6], codes[7]));
+                    g.cs[grow * nblk + gcol / 32] = (uint8_t)sb;   // cached: L2 merges the bytes of a line
                 }
             }
             __builtin_amdgcn_s_waitcnt(0);
@@ -963,7 +974,7 @@ void k_gemm_w4(GArgs g)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                    if (row < g.M && col < g.N) ((float*)g.c)[row * g.ldc + col] = acc[i][j][r] * ap;
+                    if (row < g.M && col < g.N) __builtin_nontemporal_store(acc[i][j][r] * ap, &((float*)g.c)[row * g.ldc + col]);
                 }
             }
     }
