@@ -1,20 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the MX hot path on one MI355X.
 
-One step = the whole path on one batch of synthetic input, for the MOSS
-two-level workload (M = N = K = 4096, A bf16 Student-t(3) activations with
-4 outlier K-channels x100, B bf16 N(0, 0.02) weights):
-  1. mx_quantize(A, row copy, E4M3, two-level: FP32 tensor scale + E8M0)
-  2. mx_quantize(B [K][N], column copy -> [N][K], same format)
-  3. mx_gemm(A, B) with the tensor scales applied once in the epilogue,
-     bf16 output.
+One step = the whole path on one batch of synthetic input, for one
+Llama-3-8B-shaped MLP layer's training GEMMs (tokens 8192, hidden 4096, ffn
+14336; the largest workload):
+  1. mx_quantize_dual_layout of the six operand tensors -- activations X
+     [8192][4096] and X' [8192][14336], weights W_gu [4096][28672] and W_d
+     [14336][4096] in E4M3, gradients dY_gu [8192][28672] and dY_d
+     [8192][4096] in E5M2 -- each read once and written as row and column
+     copies with E8M0 1x32 / 32x1 block scales, round to nearest even;
+  2. the six GEMMs on those copies: fprop X.W_gu, X'.W_d; dgrad dY_gu.W_gu^T,
+     dY_d.W_d^T; wgrad X^T.dY_gu, X'^T.dY_d (fp32 accumulation, bf16 out).
 Inputs are resident in HBM before timing starts; a 512 MiB read evicts
 L2/MALL before every step (outside the timed kernels) so no step reads its
 inputs from cache.  Kernel times come from HIP events recorded on the stream
 the kernels run on.
 
-Prints one JSON line (rank 0).  `--workload` selects another workload for
-profiling runs; the default is the one above.
+Prints one JSON line (rank 0).  `--workload` selects another workload (the
+MOSS two-level 4096^3 step, the FP4 wgrad step, the dual-layout quantizer
+alone, ...); the default is the one above.
 """
 import argparse
 import json
@@ -254,7 +258,6 @@ def setup_llama(args):
                       torch.empty((R, Cc // 32), dtype=torch.uint8, device="cuda"),
                       torch.empty((Cc, R), dtype=torch.uint8, device="cuda"),
                       torch.empty((Cc, R // 32), dtype=torch.uint8, device="cuda"))
-    w.tensors.clear()                         # host copies are not needed any more
     gemms, flops = [], 0.0
     for gname, an, aax, fa, bn, bax, fb in LLAMA_GEMMS:
         A, B = src[an], src[bn]
@@ -281,7 +284,7 @@ def setup_llama(args):
                 config={"workload": "llama3_8b_mlp_train", "tokens": 8192, "hidden": 4096, "ffn": 14336,
                         "gemms": [g[0] for g in gemms], "elem": "e4m3 (x, w) / e5m2 (dy)",
                         "quantizer": "dual layout, 1x32 + 32x1 e8m0", "out": "bf16"},
-                host={})
+                host=w.tensors, gemms=gemms, fmts=fmts, outs=outs)
     return step, info
 
 
@@ -337,6 +340,63 @@ def cpu_baseline_moss(host, chunk=256, budget_s=20.0):
             "sample": f"two-level quantize of full A and B ({t1 - t0:.2f} s) + {gemm_part}"}
 
 
+def cpu_baseline_llama(info, rows_per_gemm=256, per_tile=16):
+    """The oracle (plain C, all host cores) on the step: dual-layout
+    quantization of all six tensors in full, then the first
+    `rows_per_gemm` rows of C of each GEMM (the oracle's whole-matrix
+    routine on that row block), the GEMM time scaled to all rows.
+
+    Separately (not timed), 16 entries of every 128x128 output tile of each
+    GEMM, corners included, from the oracle and from the GPU's fp32-output
+    GEMM (run once) give each GEMM's largest error relative to the stated
+    bound |C - C_ref| <= 1e-5 (|A|.|B|) + 1e-6 and the fraction of entries
+    inside it."""
+    import oracle as O
+    n = os.cpu_count() or 1
+    host = info["host"]
+    t0 = time.perf_counter()
+    ora = {}
+    for name, fmt in info["fmts"].items():
+        qr, sr_, _ = O.quantize(host[name], O.AXIS_ROW, fmt, nthreads=n)
+        qc, sc, _ = O.quantize(host[name], O.AXIS_COL, fmt, nthreads=n)
+        ora[name] = {"row": (qr, sr_), "col": (qc, sc)}
+    tq = time.perf_counter() - t0
+    tg_sample, tg_full, macs = 0.0, 0.0, 0
+    for (gname, an, aax, fa, bn, bax, fb), g in zip(LLAMA_GEMMS, info["gemms"]):
+        M, N, K = g[7], g[8], g[9]
+        qao, sao = ora[an][aax]
+        qbo, sbo = ora[bn][bax]
+        r = min(rows_per_gemm, M)
+        t1 = time.perf_counter()
+        O.gemm(qao[:r], sao[:r], None, fa, qbo, sbo, None, fb, r, N, K, nthreads=n)
+        dt = time.perf_counter() - t1
+        tg_sample += dt
+        tg_full += dt * M / r
+        macs += r * N * K
+    step_s = tq + tg_full
+    base = {"value": round(info["flops"] / step_s / 1e12, 6), "unit": "TFLOP/s", "cores": n, "kind": "oracle",
+            "sample": (f"dual-layout quantization of all six tensors in full ({tq:.2f} s) + the first "
+                       f"{rows_per_gemm} rows of C of each GEMM ({macs:.3g} MACs, {tg_sample:.2f} s), GEMM "
+                       f"time scaled to all rows ({tg_full:.1f} s)")}
+    rng = np.random.default_rng(7)
+    parity = {}
+    for (gname, an, aax, fa, bn, bax, fb), g in zip(LLAMA_GEMMS, info["gemms"]):
+        _, qa, sa, _, qb, sb, _, M, N, K, _ = g
+        qao, sao = ora[an][aax]
+        qbo, sbo = ora[bn][bax]
+        ii, jj = I.sample_tile_entries(rng, M, N, per_tile)
+        Cref, bound = O.gemm_entries(qao, sao, None, fa, qbo, sbo, None, fb, M, N, K, ii, jj, nthreads=n)
+        c = mx.mx_gemm(qa, sa, None, fa, qb, sb, None, fb, M, N, K, out_dtype=mx.MX_OUT_F32)
+        got = c[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()].double().cpu().numpy()
+        del c
+        err = np.abs(got - Cref)
+        stated = 1e-5 * bound + 1e-6
+        parity[gname] = {"max_err_over_stated_bound": round(float((err / stated).max()), 4),
+                         "frac_within_stated_bound": round(float(np.mean(err <= stated)), 6),
+                         "entries": int(ii.size)}
+    return base, parity
+
+
 def measured_traffic(workload):
     """Bytes per launch of the roofline kernel if the counters match the
     current kernel source, else None."""
@@ -356,7 +416,7 @@ def main():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="moss", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="llama", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush", default="read", choices=["write", "read", "none"],
                    help="how L2/MALL are evicted before each step (outside the timed kernels); a "
@@ -428,7 +488,7 @@ def main():
     out = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "e4m3" if args.workload != "fp4" else "e2m1",
+           "dtype": {"fp4": "e2m1", "llama": "e4m3/e5m2"}.get(args.workload, "e4m3"),
            "data": "synthetic (seeded; no weights or datasets)",
            "config": info["config"], "roofline": roofline,
            "kernels": quant, "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
@@ -439,11 +499,24 @@ def main():
         out["kernels"]["gemm"] = {"ms": round(g_ms, 4), "TFLOP/s": roofline["achieved"],
                                   "frac_mfma": roofline["frac"]}
         if isinstance(info["gemm_kernel"], list):
-            for n in info["gemm_kernel"]:
-                out["kernels"][n] = {"ms": round(kernel_ms[n], 4)}
+            for g in info["gemms"]:
+                n, M, N, K = g[0], g[7], g[8], g[9]
+                tf = 2.0 * M * N * K / (kernel_ms[n] * 1e-3) / 1e12
+                out["kernels"][n] = {"ms": round(kernel_ms[n], 4), "MNK": [M, N, K], "TFLOP/s": round(tf, 1),
+                                     "frac_mfma": round(tf / MFMA_PEAK_TFLOPS[info["mfma"]], 4)}
+            out["roofline"]["algorithmic"] = (f"{info['flops']:.4g} FLOP over the six launches of one step "
+                                              "(achieved = that / the sum of their mean durations)")
+    if args.workload == "llama":
+        # the six dual quantizations against the HBM roofline; dY_gu has the
+        # element count of the standalone 16384x14336 dual-layout workload
+        out["kernels"]["dual_layout_bar"] = {"tensor": "dY_gu [8192][28672]",
+                                             "frac_hbm": quant["quant_dY_gu"]["frac_hbm"], "target": 0.70}
     if args.workload == "moss" and not args.no_cpu_baseline:
         log("timing the oracle on the host (bounded sample)")
         out["cpu_baseline"] = cpu_baseline_moss(info["host"])
+    if args.workload == "llama" and not args.no_cpu_baseline:
+        log("timing the oracle on the host (bounded sample)")
+        out["cpu_baseline"], out["gemm_parity_sampled"] = cpu_baseline_llama(info)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -75,13 +75,22 @@ __device__ __forceinline__ float tensor_scale_from_key(uint32_t key)
 
 // x / s_t rounded to nearest even, with s_t fixed for the whole tensor.  The
 // reciprocal r = RN(1/s_t) is formed once; q = RN(x r) refined by one exact
-// residual step q' = RN(q + RN(x - q s_t) r) equals the IEEE quotient
-// whenever |x|, |q'| >= 2^-96 and |q'| <= 2^17 (checked exhaustively over
-// every fp32 x for a set of divisors with adversarial significands).  Per
-// block the kernels check |x| >= T = max(2^-96, 2^-95 |s_t|) for every
-// nonzero x (which implies |q'| >= 2^-96) and |q'| <= 2^17 on the block's
-// largest quotient; a block that fails takes the IEEE division.  Zeros keep
-// the sign of x r; a non-finite x makes the block non-finite either way.
+// residual step q' = RN(q + RN(x - q s_t) r) equals the IEEE quotient.  This
+// is Markstein's correction theorem (P. Markstein, IBM J. Res. Dev. 34(1),
+// 1990; Theorem 8.10 of Muller et al., Handbook of Floating-Point
+// Arithmetic): if r is within half an ulp of 1/s_t (here r = RN(1/s_t))
+// and q within one ulp of x/s_t (q = RN(x r) is: the reciprocal's half-ulp
+// error and the product's rounding stay below one ulp), the residual
+// x - q s_t is exactly representable and one FMA returns RN(x/s_t) --
+// provided nothing underflows or overflows along the way.  The range checks
+// keep away from those cases: the kernels require |x|, |q'| >= 2^-96 and
+// |q'| <= 2^17 (the range over which the identity was also checked
+// exhaustively, every fp32 x against divisors with adversarial
+// significands).  Per block they check |x| >= T = max(2^-96, 2^-95 |s_t|)
+// for every nonzero x (which implies |q'| >= 2^-96) and |q'| <= 2^17 on the
+// block's largest quotient; a block that fails takes the IEEE division.
+// Zeros keep the sign of x r; a non-finite x makes the block non-finite
+// either way.
 struct TensorDiv {
     float s, r;
     uint32_t lo_key;    // (bits(T) << 1) - 1
@@ -961,10 +970,13 @@ hipError_t launch_fmt(const QuantJob& j, hipStream_t stream)
 
 }  // namespace
 
+// partial maxima per tensor of the prediction (W's in work[0, 512), g's in
+// work[512, 1024)): at most one workgroup per 2048 16-byte words
+constexpr int kPredictPartials = 512;
+
 template <int SRC, int FMT>
 hipError_t launch_predict_t(const PredictJob& j, hipStream_t stream)
 {
-    // partial maxima of W in work[0, 512), of g in work[512, 1024)
     constexpr int es = SrcT<SRC>::bytes;
     int n[2], flat[2];
     const void* src[2] = {j.w, j.g};
@@ -973,11 +985,12 @@ hipError_t launch_predict_t(const PredictJob& j, hipStream_t stream)
         flat[t] = ((reinterpret_cast<uintptr_t>(src[t]) & 15u) == 0) && ld[t] == j.cols && (j.cols * es) % 16 == 0;
         const int64_t nwords = j.rows * j.cols * es / 16;
         int64_t want = flat[t] ? (nwords + 2047) / 2048 : j.rows;
-        n[t] = (int)(want < 1 ? 1 : (want > 512 ? 512 : want));
+        n[t] = (int)(want < 1 ? 1 : (want > kPredictPartials ? kPredictPartials : want));
     }
     k_amax_partial2<SRC><<<dim3((unsigned)(n[0] + n[1])), dim3(256), 0, stream>>>(
-        j.w, j.ld_w, flat[0], j.work, n[0], j.g, j.ld_g, flat[1], j.work + 512, j.rows, j.cols);
-    k_predict_scale<FMT><<<dim3(1), dim3(256), 0, stream>>>(j.work, n[0], j.work + 512, n[1], j.lr, j.scale_out);
+        j.w, j.ld_w, flat[0], j.work, n[0], j.g, j.ld_g, flat[1], j.work + kPredictPartials, j.rows, j.cols);
+    k_predict_scale<FMT><<<dim3(1), dim3(256), 0, stream>>>(j.work, n[0], j.work + kPredictPartials, n[1], j.lr,
+                                                            j.scale_out);
     return hipGetLastError();
 }
 

@@ -150,3 +150,23 @@ def sample_blocks(rng: np.random.Generator, rows: int, cols: int, axis: int, n: 
             r = np.concatenate([r, [0, 0, rows - 32, rows - 32]])
             c = np.concatenate([c, [0, cols - 1, 0, cols - 1]])
     return r.astype(np.int64), c.astype(np.int64)
+
+
+def sample_tile_entries(rng: np.random.Generator, M: int, N: int, per_tile: int = 16,
+                        tile: int = 128) -> Tuple[np.ndarray, np.ndarray]:
+    """Output entries (ii, jj) of an M x N matrix for a stratified check: in
+    every tile x tile block (ragged edge blocks included) its four corners
+    plus per_tile - 4 uniformly drawn entries."""
+    ti = np.arange(0, M, tile)
+    tj = np.arange(0, N, tile)
+    r0 = np.repeat(ti, len(tj))
+    c0 = np.tile(tj, len(ti))
+    r1 = np.minimum(r0 + tile, M) - 1
+    c1 = np.minimum(c0 + tile, N) - 1
+    nt = r0.size
+    extra = per_tile - 4
+    rr = r0[:, None] + (rng.random((nt, extra)) * (r1 - r0 + 1)[:, None]).astype(np.int64)
+    cc = c0[:, None] + (rng.random((nt, extra)) * (c1 - c0 + 1)[:, None]).astype(np.int64)
+    ii = np.concatenate([np.stack([r0, r0, r1, r1], 1), rr], 1).ravel()
+    jj = np.concatenate([np.stack([c0, c1, c0, c1], 1), cc], 1).ravel()
+    return ii.astype(np.int64), jj.astype(np.int64)

@@ -214,8 +214,10 @@ mx_status mx_dequantize(const void* q, const uint8_t* scales, const float* tenso
  *     scale_out = RN(RN(max|W| + RN(lr * max|g|)) / Fmax(fmt))
  * -- product, sum and IEEE division each rounded once, in that order
  * (the page's int8 illustration divides by 127; Fmax is 448 / 57344 / 6).
- * 1 when the sum is 0; NaN when W or g holds a NaN; +Inf when one holds
- * an Inf.  Pass the result to mx_quantize / mx_quantize_dual_layout with
+ * 1 when the sum is 0.  Non-finite inputs follow IEEE arithmetic: NaN
+ * when W or g holds a NaN, and when lr == 0 and g holds an Inf (0 * Inf);
+ * otherwise +Inf when W or g holds an Inf.  Pass the result to
+ * mx_quantize / mx_quantize_dual_layout with
  * MX_SCALE_E8M0_TENSOR_F32 and MX_TSCALE_PROVIDED for W'.
  *
  * w, g:   device tensors of `src_dtype`, both rows x cols, row strides

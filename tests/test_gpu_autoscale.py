@@ -61,10 +61,13 @@ def test_strided_views_and_special_values():
     gn[7, 9] = np.nan
     wi = one.copy()
     wi[1, 2] = -np.inf
-    for a, b in [(z, z), (one, z), (one, gn), (wi, z)]:
-        got = mx.mx_predict_tensor_scale(to_device(a), to_device(b), 0.5, "e4m3")
+    gi = z.copy()
+    gi[5, 6] = np.inf
+    for a, b, lr in [(z, z, 0.5), (one, z, 0.5), (one, gn, 0.5), (wi, z, 0.5), (one, gi, 0.5), (one, gi, 0.0),
+                     (wi, z, 0.0)]:
+        got = mx.mx_predict_tensor_scale(to_device(a), to_device(b), lr, "e4m3")
         torch.cuda.synchronize()
-        _same(got.item(), O.predict_tensor_scale(a, b, 0.5, "e4m3"))
+        _same(got.item(), O.predict_tensor_scale(a, b, lr, "e4m3"))
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])

@@ -11,8 +11,8 @@ import torch
 import oracle as O
 from fp4_quantization_block_amd import inputs as I
 from fp4_quantization_block_amd import mx
-from gpu_util import (DEV, assert_codes_equal, gemm_check, log, mfma_allowance,
-                      mfma_allowance_entries, mfma_model, require_gpu, to_device, u8)
+from gpu_util import (DEV, assert_codes_equal, check_model, gemm_check, log, mfma_rule, record,
+                      require_gpu, tile_samples, to_device, u8)
 
 pytestmark = pytest.mark.gpu
 SEED = I.SR_SEED
@@ -78,13 +78,9 @@ def test_gemm_small(case):
     allow = None
     if O.elem_bits(fa) == 8:
         ap = _alpha_prime(alpha, tao, tbo, hk)
-        allow = mfma_allowance(O.unpack_codes(qao, fa), sao, fa, O.unpack_codes(qbo, fb), sbo, fb, ap)
+        model, allow = mfma_rule(O.unpack_codes(qao, fa), sao, fa, O.unpack_codes(qbo, fb), sbo, fb, ap)
         if out == "f32":
-            # the kernel computes exactly what the matrix cores define
-            model = mfma_model(O.unpack_codes(qao, fa), sao, fa, O.unpack_codes(qbo, fb), sbo, fb, ap)
-            dev_ = np.abs(got - model)
-            lim = (K / 64 + 2) * 2.0 ** -24 * bound + 1e-30
-            assert np.all(dev_ <= lim), f"{name}: kernel differs from the MFMA arithmetic by {np.max(dev_ / lim):.2f}x"
+            check_model(got, model, bound, K, name)   # the kernel computes what the matrix cores define
     r = gemm_check(got, C, bound, out == "bf16", name, allow)
     log(f"{name}: (max err / stated tol, fraction within stated tol) = {r}")
 
@@ -112,14 +108,10 @@ def test_gemm_ldc(K):
     torch.cuda.synchronize()
     C, bound = O.gemm(qao, sao, None, "e4m3", qbo, sbo, None, "e4m3", M, N, K)
     g = big.cpu().numpy()
-    gemm_check(g[:, :N], C, bound, False, "ldc", mfma_allowance(qao, sao, "e4m3", qbo, sbo, "e4m3", 1.0))
+    model, allow = mfma_rule(qao, sao, "e4m3", qbo, sbo, "e4m3", 1.0)
+    gemm_check(g[:, :N], C, bound, False, "ldc", allow)
+    check_model(g[:, :N], model, bound, K, "ldc")
     assert np.all(g[:, N:] == 7.0)                      # outside N untouched
-
-
-def _sample_entries(rng, M, N, n):
-    ii = np.concatenate([rng.integers(0, M, n), [0, 0, M - 1, M - 1]])
-    jj = np.concatenate([rng.integers(0, N, n), [0, N - 1, 0, N - 1]])
-    return ii, jj
 
 
 def _pick(c, ii, jj):
@@ -127,20 +119,45 @@ def _pick(c, ii, jj):
     return t.float().cpu().numpy().astype(np.float64)
 
 
+def _report(config, gemm, shape, fa, fb, got, C, bound, K, ap, qa_u=None, sa=None, qb_u=None, sb=None,
+            ii=None, jj=None, sampled="all outputs"):
+    """fp32-output parity of one GEMM against the oracle, and a record of
+    its largest error relative to the stated bound and the fraction of
+    outputs inside that bound.  FP8: the stated bound plus the MFMA rule's
+    worst-case truncation, and agreement with the rule up to fp32
+    accumulation.  FP4: the stated bound alone."""
+    entry = {"config": config, "gemm": gemm, "shape_MNK": list(shape), "formats": [fa, fb],
+             "checked": sampled, "n": int(np.size(got))}
+    if O.elem_bits(fa) == 8:
+        model, allow = mfma_rule(qa_u, sa, fa, qb_u, sb, fb, ap, ii, jj)
+        entry["max_dev_vs_rule_over_accum_limit"] = check_model(got, model, bound, K, f"{config} {gemm}")
+        ratio, frac = gemm_check(got, C, bound, False, f"{config} {gemm}", allow)
+    else:
+        ratio, frac = gemm_check(got, C, bound, False, f"{config} {gemm}")
+    entry["max_err_over_stated_bound"] = ratio
+    entry["frac_within_stated_bound"] = frac
+    log(f"{config} {gemm} {shape}: max err / stated bound {ratio:.3f}, within stated bound {frac:.4%} "
+        f"({sampled}, {entry['n']} entries)")
+    record(entry)
+    return entry
+
+
 def test_full_mxfp8_gemm_256():
     w = I.make("mxfp8_gemm_256")
     (qa, sa, _), (qao, sao, _) = quant_both(w.tensors["A"], O.AXIS_ROW, "e4m3")
     (qb, sb, _), (qbo, sbo, _) = quant_both(w.tensors["B"], O.AXIS_COL, "e4m3")
-    allow = mfma_allowance(qao, sao, "e4m3", qbo, sbo, "e4m3", 1.0)
-    for od in (mx.MX_OUT_F32, mx.MX_OUT_BF16):
-        c = mx.mx_gemm(qa, sa, None, "e4m3", qb, sb, None, "e4m3", 256, 256, 256, out_dtype=od)
-        torch.cuda.synchronize()
-        C, bound = O.gemm(qao, sao, None, "e4m3", qbo, sbo, None, "e4m3", 256, 256, 256)
-        r = gemm_check(c.float().cpu().numpy(), C, bound, od == mx.MX_OUT_BF16, "256^3", allow)
-        log("256^3 (max err / stated tol, fraction within stated tol)", r)
+    C, bound = O.gemm(qao, sao, None, "e4m3", qbo, sbo, None, "e4m3", 256, 256, 256)
+    c32 = mx.mx_gemm(qa, sa, None, "e4m3", qb, sb, None, "e4m3", 256, 256, 256, out_dtype=mx.MX_OUT_F32)
+    c16 = mx.mx_gemm(qa, sa, None, "e4m3", qb, sb, None, "e4m3", 256, 256, 256, out_dtype=mx.MX_OUT_BF16)
+    torch.cuda.synchronize()
+    _report("mxfp8_256", "gemm", (256, 256, 256), "e4m3", "e4m3", c32.cpu().numpy(), C, bound, 256, 1.0,
+            qao, sao, qbo, sbo)
+    allow = mfma_rule(qao, sao, "e4m3", qbo, sbo, "e4m3", 1.0)[1]
+    gemm_check(c16.float().cpu().numpy(), C, bound, True, "256^3 bf16", allow)
 
 
-def test_full_moss_two_level_4096_sampled():
+def test_full_moss_two_level_4096():
+    """Every output of the 4096^3 two-level GEMM, fp32 and bf16."""
     w = I.make("moss_two_level_4096")
     (qa, sa, ta), (qao, sao, tao) = quant_both(w.tensors["A"], O.AXIS_ROW, "e4m3", two_level=True)
     (qb, sb, tb), (qbo, sbo, tbo) = quant_both(w.tensors["B"], O.AXIS_COL, "e4m3", two_level=True)
@@ -148,16 +165,17 @@ def test_full_moss_two_level_4096_sampled():
     c32 = mx.mx_gemm(qa, sa, ta, "e4m3", qb, sb, tb, "e4m3", n, n, n, out_dtype=mx.MX_OUT_F32)
     c16 = mx.mx_gemm(qa, sa, ta, "e4m3", qb, sb, tb, "e4m3", n, n, n, out_dtype=mx.MX_OUT_BF16)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(22)
-    ii, jj = _sample_entries(rng, n, n, 4000)
-    C, bound = O.gemm_entries(qao, sao, tao, "e4m3", qbo, sbo, tbo, "e4m3", n, n, n, ii, jj)
-    allow = mfma_allowance_entries(qao, sao, "e4m3", qbo, sbo, "e4m3", float(tao) * float(tbo), ii, jj)
-    r = gemm_check(_pick(c32, ii, jj), C, bound, False, "4096^3 two-level fp32", allow)
-    log("4096^3 (max err / stated tol, fraction within stated tol)", r)
-    gemm_check(_pick(c16, ii, jj), C, bound, True, "4096^3 two-level bf16", allow)
+    C, bound = O.gemm(qao, sao, tao, "e4m3", qbo, sbo, tbo, "e4m3", n, n, n)
+    ap = float(np.float32(tao)) * float(np.float32(tbo))
+    _report("moss_two_level_4096", "gemm", (n, n, n), "e4m3", "e4m3", c32.cpu().numpy(), C, bound, n, ap,
+            qao, sao, qbo, sbo)
+    allow = mfma_rule(qao, sao, "e4m3", qbo, sbo, "e4m3", ap)[1]
+    gemm_check(c16.float().cpu().numpy(), C, bound, True, "4096^3 two-level bf16", allow)
 
 
-def test_full_mxfp4_wgrad_sampled():
+def test_full_mxfp4_wgrad():
+    """Every output of the FP4 wgrad GEMM (M 6144, N 4096, K 16384) against
+    the stated bound alone (FP4 products are exact)."""
     w = I.make("mxfp4_wgrad_qkv")
     dY, X = w.tensors["dY"], w.tensors["X"]        # [T][Q], [T][H]; K = T
     T, Q = dY.shape
@@ -167,12 +185,10 @@ def test_full_mxfp4_wgrad_sampled():
     c = mx.mx_gemm(qa, sa, None, "e2m1", qb, sb, None, "e2m1", Q, H, T, hadamard_k=True,
                    out_dtype=mx.MX_OUT_F32)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(21)
-    ii, jj = _sample_entries(rng, Q, H, 3000)
-    C, bound = O.gemm_entries(qao, sao, None, "e2m1", qbo, sbo, None, "e2m1", Q, H, T, ii, jj,
-                              hadamard_k=True)
-    r = gemm_check(_pick(c, ii, jj), C, bound, False, "fp4 wgrad")
-    log("fp4 wgrad max err/tol", r)
+    got = c.cpu().numpy()
+    del c
+    C, bound = O.gemm(qao, sao, None, "e2m1", qbo, sbo, None, "e2m1", Q, H, T, hadamard_k=True)
+    _report("mxfp4_wgrad_qkv", "wgrad", (Q, H, T), "e2m1", "e2m1", got, C, bound, T, 1.0 / 32)
 
 
 def quant_both_sampled(x, fmt):
@@ -195,57 +211,43 @@ MLP = [  # (name, A tensor, A axis, fa, B tensor, B axis, fb)
     ("wgrad_gate_up", "X", "col", "e4m3", "dY_gu", "col", "e5m2"),
     ("wgrad_down", "Xp", "col", "e4m3", "dY_d", "col", "e5m2"),
 ]
+MLP_FMTS = {"X": "e4m3", "Xp": "e4m3", "W_gu": "e4m3", "W_d": "e4m3", "dY_gu": "e5m2", "dY_d": "e5m2"}
 
 
-def test_full_llama3_8b_mlp_sampled():
-    """The six training GEMMs from dual-layout operands (each source tensor
-    read once); each checked on sampled entries against the oracle."""
+def test_full_llama3_8b_mlp():
+    """The Llama-3-8B MLP training step: all six dual-layout quantizations
+    compared in full (both copies, codes and scales), then the six GEMMs
+    from those operands, each checked on 16 entries of every 128x128 output
+    tile (its four corners included) against the oracle and the MFMA rule."""
     w = I.make("llama3_8b_mlp")
-    fmts = {"X": "e4m3", "Xp": "e4m3", "W_gu": "e4m3", "W_d": "e4m3", "dY_gu": "e5m2", "dY_d": "e5m2"}
-    dev = {}
-    for name, fmt in fmts.items():
-        qr, sr_, qc, sc, _ = mx.mx_quantize_dual_layout(to_device(w.tensors[name]), mx.qconfig(fmt))
+    dev, ora = {}, {}
+    for name, fmt in MLP_FMTS.items():
+        x = w.tensors[name]
+        qr, sr_, qc, sc, _ = mx.mx_quantize_dual_layout(to_device(x), mx.qconfig(fmt))
+        torch.cuda.synchronize()
+        qro, sro, _ = O.quantize(x, O.AXIS_ROW, fmt)
+        qco, sco, _ = O.quantize(x, O.AXIS_COL, fmt)
+        assert_codes_equal(u8(qr), qro, f"{name} row codes")
+        assert_codes_equal(u8(sr_), sro, f"{name} row scales")
+        assert_codes_equal(u8(qc), qco, f"{name} col codes")
+        assert_codes_equal(u8(sc), sco, f"{name} col scales")
         dev[name] = {"row": (qr, sr_), "col": (qc, sc)}
-    torch.cuda.synchronize()
+        ora[name] = {"row": (qro, sro), "col": (qco, sco)}
+        log(f"mlp {name} {x.shape}: both copies equal the oracle's")
+    w.tensors.clear()
     rng = np.random.default_rng(23)
     for gname, an, aax, fa, bn, bax, fb in MLP:
-        A, B = w.tensors[an], w.tensors[bn]
         qa, sa = dev[an][aax]
         qb, sb = dev[bn][bax]
-        M = A.shape[0] if aax == "row" else A.shape[1]
-        K = A.shape[1] if aax == "row" else A.shape[0]
-        N = B.shape[1] if bax == "col" else B.shape[0]
+        qao, sao = ora[an][aax]
+        qbo, sbo = ora[bn][bax]
+        M, K = qao.shape
+        N = qbo.shape[0]
         c = mx.mx_gemm(qa, sa, None, fa, qb, sb, None, fb, M, N, K, out_dtype=mx.MX_OUT_F32)
         torch.cuda.synchronize()
-        ii, jj = _sample_entries(rng, M, N, 600)
-        # oracle operands: only the rows the sampled entries touch
-        ua, ia = np.unique(ii, return_inverse=True)
-        ub, ib = np.unique(jj, return_inverse=True)
-        qao, sao = _oracle_rows(A, aax, fa, ua)
-        qbo, sbo = _oracle_rows(B, bax, fb, ub)
-        C, bound = O.gemm_entries(qao, sao, None, fa, qbo, sbo, None, fb, len(ua), len(ub), K,
-                                  ia, ib)
-        allow = mfma_allowance_entries(qao, sao, fa, qbo, sbo, fb, 1.0, ia, ib)
-        r = gemm_check(_pick(c, ii, jj), C, bound, False, gname, allow)
-        log(f"{gname} ({M},{N},{K}) max err/tol {r}")
+        ii, jj = tile_samples(rng, M, N)
+        got = _pick(c, ii, jj)
         del c
-
-
-def _oracle_rows(x, axis, fmt, rows):
-    """Oracle-quantized stored rows `rows` of a copy (row copy: source rows;
-    column copy: source columns), packed as the quantizer writes them."""
-    R, Cc = x.shape
-    if axis == "row":
-        r0 = np.repeat(rows, Cc // 32)
-        c0 = np.tile(np.arange(0, Cc, 32), len(rows))
-        codes, scales = O.quantize_blocks(x, O.AXIS_ROW, fmt, r0, c0)
-        kblk = Cc // 32
-    else:
-        c0 = np.repeat(rows, R // 32)
-        r0 = np.tile(np.arange(0, R, 32), len(rows))
-        codes, scales = O.quantize_blocks(x, O.AXIS_COL, fmt, r0, c0)
-        kblk = R // 32
-    codes = codes.reshape(len(rows), kblk * 32)
-    if O.elem_bits(fmt) == 4:
-        codes = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    return codes, scales.reshape(len(rows), kblk)
+        C, bound = O.gemm_entries(qao, sao, None, fa, qbo, sbo, None, fb, M, N, K, ii, jj)
+        _report("llama3_8b_mlp", gname, (M, N, K), fa, fb, got, C, bound, K, 1.0, qao, sao, qbo, sbo, ii, jj,
+                sampled="16 per 128x128 tile incl. corners")

@@ -80,6 +80,11 @@ def test_special_values():
     wi = w.copy()
     wi[0, 0] = np.inf
     assert O.predict_tensor_scale(wi, z, 0.5, "e4m3") == np.inf
+    gi = z.copy()
+    gi[1, 1] = -np.inf
+    assert O.predict_tensor_scale(w, gi, 0.5, "e4m3") == np.inf       # lr * Inf = Inf
+    assert np.isnan(O.predict_tensor_scale(w, gi, 0.0, "e4m3"))       # lr = 0: 0 * Inf = NaN (IEEE)
+    assert O.predict_tensor_scale(wi, z, 0.0, "e4m3") == np.inf       # an Inf weight stays Inf
     # a provided scale from the prediction quantizes like any provided scale
     rng = np.random.default_rng(9)
     w2, g2 = _pair(rng, 32, 64, "f32")

@@ -237,3 +237,43 @@ def test_dequantize_inverts_quantize_within_half_step(fmt):
             mb = {O.E4M3: 3, O.E5M2: 2, O.E2M1: 1}[fmt]
             tol = np.abs(x).max() * 2.0 ** (-mb) * (6.0 if had else 1.0)
             assert err.max() <= tol
+
+
+@pytest.mark.parametrize("axis", [O.AXIS_ROW, O.AXIS_COL])
+def test_dequantize_hadamard_tensor_scale_exact(axis):
+    """The Hadamard + tensor-scale branch of dequantize on a case whose
+    every intermediate is exact: small-integer E4M3 codes, power-of-two
+    block scales, so x_hat, H.x_hat (scipy's Sylvester matrix) and the 1/32
+    are exact and the result is one rounding of H.x_hat/32 * s_t.  With an
+    s_t of long significand this fixes the order (inverse transform first,
+    then the tensor scale once): scaling each element before the transform
+    gives different bits."""
+    scipy_linalg = pytest.importorskip("scipy.linalg")
+    H = scipy_linalg.hadamard(32).astype(np.float64)
+    rng = np.random.default_rng(12)
+    rows, cols = 64, 96
+    v = rng.integers(-15, 16, (rows, cols)).astype(np.float64)     # exact in E4M3
+    codes = np.array([O.encode_rne(O.E4M3, t) for t in v.ravel()], np.uint8).reshape(rows, cols)
+    st = np.float32(0.1)
+    if axis == O.AXIS_ROW:
+        bytes_ = rng.integers(124, 131, (rows, cols // 32)).astype(np.uint8)
+        xhat = v * np.exp2(np.repeat(bytes_, 32, 1).astype(np.float64) - 127)
+        blocks = xhat.reshape(rows, cols // 32, 32)
+        exact = np.einsum("ij,rbj->rbi", H, blocks).reshape(rows, cols) / 32
+        q, s = codes, bytes_
+    else:
+        bytes_ = rng.integers(124, 131, (cols, rows // 32)).astype(np.uint8)      # [col][row block]
+        xhat = v * np.exp2(np.repeat(bytes_.T, 32, 0).astype(np.float64) - 127)
+        blocks = xhat.reshape(rows // 32, 32, cols)
+        exact = np.einsum("ij,bjc->bic", H, blocks).reshape(rows, cols) / 32
+        q, s = np.ascontiguousarray(codes.T), bytes_
+    got = O.dequantize(q, s, float(st), O.E4M3, rows, cols, axis, hadamard=True)
+    want = (exact * np.float64(st)).astype(np.float32)              # one rounding of an exact product
+    assert np.array_equal(got, want)
+    # the other order: each element scaled (rounded) first, then the transform
+    xs = (xhat * np.float64(st)).astype(np.float32).astype(np.float64)
+    if axis == O.AXIS_ROW:
+        other = np.einsum("ij,rbj->rbi", H, xs.reshape(rows, cols // 32, 32)).reshape(rows, cols) / 32
+    else:
+        other = np.einsum("ij,bjc->bic", H, xs.reshape(rows // 32, 32, cols)).reshape(rows, cols) / 32
+    assert not np.array_equal(got, other.astype(np.float32))
