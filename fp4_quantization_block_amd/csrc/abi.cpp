@@ -158,6 +158,26 @@ mx_status mx_predict_tensor_scale(const void* w, int64_t ld_w, const void* g, in
     return hip_status(mx::launch_predict(j, (hipStream_t)stream));
 }
 
+mx_status mx_predict_tensor_scale_noalloc(const void* w, int64_t ld_w, const void* g, int64_t ld_g,
+                                          int32_t src_dtype, int64_t rows, int64_t cols, float lr,
+                                          int32_t fmt, float* scale_out, void* stream)
+{
+    g_msg[0] = '\0';
+    mx_status s = check_source(w, src_dtype, rows, cols, ld_w);
+    if (s != MX_OK) return s;
+    if ((s = check_source(g, src_dtype, rows, cols, ld_g)) != MX_OK) return s;
+    if (!valid_fmt(fmt)) return fail(MX_ERR_INVALID_ARG, "unknown element format");
+    if (!(lr >= 0.0f) || lr > 3.4028234663852886e38f) return fail(MX_ERR_INVALID_ARG, "lr must be finite and >= 0");
+    if (!scale_out) return fail(MX_ERR_INVALID_ARG, "scale_out must not be NULL");
+    if (reinterpret_cast<uintptr_t>(scale_out) & 3u) return fail(MX_ERR_ALIGNMENT, "scale_out must be 4-byte aligned");
+    mx::PredictJob j{};
+    j.w = w; j.g = g; j.src = src_dtype;
+    j.rows = rows; j.cols = cols; j.ld_w = ld_w; j.ld_g = ld_g;
+    j.lr = lr; j.fmt = fmt;
+    j.scale_out = scale_out;
+    return hip_status(mx::launch_predict_noalloc(j, (hipStream_t)stream));
+}
+
 namespace {
 
 mx_status check_gemm_operands(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,

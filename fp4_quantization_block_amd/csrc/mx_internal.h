@@ -35,6 +35,8 @@ struct PredictJob {
 };
 
 hipError_t launch_predict(const PredictJob& j, hipStream_t stream);
+// the same with the library's own per-device scratch in place of j.work
+hipError_t launch_predict_noalloc(PredictJob j, hipStream_t stream);
 
 struct DequantJob {
     const uint8_t* q; const uint8_t* scales; const float* tensor_scale;

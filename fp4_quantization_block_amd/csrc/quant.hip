@@ -35,6 +35,8 @@
 //                 writes s_t = amax / Fmax.  The partials are parked in the
 //                 caller's scale array, which the quantize kernel overwrites
 //                 afterwards (no atomics, no extra memory).
+#include <mutex>
+
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -992,6 +994,60 @@ hipError_t launch_predict_t(const PredictJob& j, hipStream_t stream)
     k_predict_scale<FMT><<<dim3(1), dim3(256), 0, stream>>>(j.work, n[0], j.work + kPredictPartials, n[1], j.lr,
                                                             j.scale_out);
     return hipGetLastError();
+}
+
+// Scratch of the no-allocation prediction entry point: the partial maxima
+// of W (words [0, 512)) and of g (words [512, 1024)), the same layout the
+// caller's workspace has in mx_predict_tensor_scale.  Each GPU holds its
+// own copy until the process ends; every call on that GPU shares it, so
+// calls that overlap on one GPU race.  Nothing in it needs clearing: each
+// call writes every partial word it then reads.
+constexpr int kPredictScratchWords = 2 * kPredictPartials;
+__device__ __align__(256) uint32_t scratch[kPredictScratchWords];
+
+namespace {
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+uint32_t* g_scratch[kMaxDevices] = {};
+
+// The device address of `scratch` on the device that owns `stream`, looked
+// up once per device (with that device current) and kept: host code never
+// passes the array's own name, which on the host is only a stand-in.
+hipError_t scratch_on(hipStream_t stream, uint32_t** out)
+{
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (stream) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = dev != cur ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (back != hipSuccess) return back;
+        g_scratch[dev] = (uint32_t*)p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_predict_noalloc(PredictJob j, hipStream_t stream)
+{
+    // the partial counts are capped at kPredictPartials per tensor
+    // (launch_predict_t), so every input size fits the scratch words
+    uint32_t* p = nullptr;
+    const hipError_t e = scratch_on(stream, &p);
+    if (e != hipSuccess) return e;
+    j.work = p;
+    return launch_predict(j, stream);
 }
 
 hipError_t launch_predict(const PredictJob& j, hipStream_t stream)

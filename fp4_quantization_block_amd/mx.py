@@ -26,7 +26,8 @@ MX_OUT_F32, MX_OUT_BF16 = 0, 1
 FMTS = {"e4m3": MX_E4M3, "e5m2": MX_E5M2, "e2m1": MX_E2M1}
 EXPORTED = ("mx_quantize", "mx_quantize_dual_layout", "mx_gemm", "mx_dequantize",
             "mx_status_string", "mx_last_error_message",
-            "mx_predict_tensor_scale", "mx_predict_workspace_bytes", "mx_gemm_quantized")
+            "mx_predict_tensor_scale", "mx_predict_workspace_bytes", "mx_gemm_quantized",
+            "mx_predict_tensor_scale_noalloc")
 
 
 class MXError(RuntimeError):
@@ -73,6 +74,9 @@ def load() -> ctypes.CDLL:
     L.mx_predict_tensor_scale.restype = _i32
     L.mx_predict_tensor_scale.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, ctypes.c_float, _i32,
                                           _vp, _i64, _vp, _vp]
+    L.mx_predict_tensor_scale_noalloc.restype = _i32
+    L.mx_predict_tensor_scale_noalloc.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, ctypes.c_float,
+                                                  _i32, _vp, _vp]
     L.mx_predict_workspace_bytes.restype = _i64
     L.mx_predict_workspace_bytes.argtypes = []
     L.mx_status_string.restype = ctypes.c_char_p
@@ -220,6 +224,21 @@ def mx_predict_tensor_scale(w: torch.Tensor, g: torch.Tensor, lr: float, fmt,
     _check(load().mx_predict_tensor_scale(_ptr(w), w.stride(0), _ptr(g), g.stride(0), src, rows, cols,
                                           float(lr), _fmt(fmt), _ptr(work), work.numel() * work.element_size(),
                                           _ptr(scale_out), _stream(stream)))
+    return scale_out
+
+
+def mx_predict_tensor_scale_noalloc(w: torch.Tensor, g: torch.Tensor, lr: float, fmt,
+                                    scale_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """mx_predict_tensor_scale without a workspace: the library's per-GPU
+    scratch holds the partial maxima (calls overlapping on one GPU race)."""
+    src = _src(w)
+    if _src(g) != src or tuple(g.shape) != tuple(w.shape):
+        raise ValueError("w and g must have the same dtype and shape")
+    rows, cols = w.shape
+    if scale_out is None:
+        scale_out = torch.empty(1, dtype=torch.float32, device=w.device)
+    _check(load().mx_predict_tensor_scale_noalloc(_ptr(w), w.stride(0), _ptr(g), g.stride(0), src, rows, cols,
+                                                  float(lr), _fmt(fmt), _ptr(scale_out), _stream(stream)))
     return scale_out
 
 

@@ -13,7 +13,9 @@
  *
  * Conventions for every call
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
- *     library allocates no memory and keeps no state between calls.
+ *     library allocates no memory and keeps no state between calls, with
+ *     one exception: the 4 KiB per-GPU scratch array of
+ *     mx_predict_tensor_scale_noalloc (see there).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
  *     only enqueues work on it and returns without synchronizing; outputs
  *     are valid once the stream reaches that point.
@@ -239,6 +241,28 @@ mx_status mx_predict_tensor_scale(const void* w, int64_t ld_w, const void* g, in
 
 /* Bytes of workspace mx_predict_tensor_scale needs (a constant, 4096). */
 int64_t mx_predict_workspace_bytes(void);
+
+/*
+ * mx_predict_tensor_scale_noalloc -- mx_predict_tensor_scale for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): no `work` argument, and
+ * the call allocates nothing.  Same arguments (minus work / work_bytes),
+ * result and errors as mx_predict_tensor_scale, computed by the same
+ * kernels.
+ *
+ * The partial maxima go to a 4 KiB scratch array the library holds in each
+ * GPU's memory from the first call on that GPU until the process ends (its
+ * device address is looked up once per GPU).  Every input size fits it: at
+ * most 512 partial maxima per tensor are kept whatever the shape, so no
+ * size is rejected for the scratch.  Each call writes every scratch word it
+ * then reads, so nothing needs clearing between calls, but all calls on one
+ * GPU share the array: calls that overlap on one GPU (different streams,
+ * or different host threads) race and must be ordered by the caller.
+ * `stream` may belong to any GPU; the scratch of that GPU is used.
+ */
+mx_status mx_predict_tensor_scale_noalloc(const void* w, int64_t ld_w, const void* g, int64_t ld_g,
+                                          int32_t src_dtype, int64_t rows, int64_t cols, float lr,
+                                          int32_t fmt, float* scale_out, void* stream);
 
 /* Static text for a status code. */
 const char* mx_status_string(mx_status status);

@@ -183,3 +183,29 @@ def _gemmq(lib, M=64, N=64, K=128, fa=0, fb=0, out_fmt=0, qc=None, sc=None, sa=N
 def test_gemm_quantized_validation(lib, kw, status):
     assert _gemmq(lib, **kw) == status
     assert lib.mx_last_error_message().decode() != ""
+
+
+def _predict_noalloc(lib, w=None, ldw=64, g=None, ldg=64, src=1, rows=64, cols=64, lr=1e-3, fmt=0, out=None):
+    FAKE = ctypes.c_void_p(0x10000)
+    return lib.mx_predict_tensor_scale_noalloc(FAKE if w is None else w, ldw, FAKE if g is None else g, ldg, src,
+                                               rows, cols, lr, fmt, FAKE if out is None else out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=ctypes.c_void_p(0)), mx.MX_ERR_INVALID_ARG),
+    (dict(g=ctypes.c_void_p(0)), mx.MX_ERR_INVALID_ARG),
+    (dict(out=ctypes.c_void_p(0)), mx.MX_ERR_INVALID_ARG),
+    (dict(src=7), mx.MX_ERR_INVALID_ARG),
+    (dict(fmt=9), mx.MX_ERR_INVALID_ARG),
+    (dict(cols=0), mx.MX_ERR_INVALID_ARG),
+    (dict(ldg=63), mx.MX_ERR_INVALID_ARG),
+    (dict(lr=-1e-3), mx.MX_ERR_INVALID_ARG),
+    (dict(lr=float("nan")), mx.MX_ERR_INVALID_ARG),
+    (dict(out=ctypes.c_void_p(0x10001)), mx.MX_ERR_ALIGNMENT),
+    (dict(g=ctypes.c_void_p(0x10001)), mx.MX_ERR_ALIGNMENT),
+])
+def test_predict_tensor_scale_noalloc_validation(lib, kw, status):
+    """The no-allocation variant validates like the workspace version (no
+    HIP call is made for any of these)."""
+    assert _predict_noalloc(lib, **kw) == status
+    assert lib.mx_last_error_message().decode() != ""
