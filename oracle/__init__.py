@@ -84,6 +84,14 @@ def _load():
     L.or_gemm_entries.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, ctypes.c_int,
                                   _i64, _i64, _i64, ctypes.c_double, ctypes.c_int, _vp, _vp,
                                   _i64, _vp, _vp, ctypes.c_int]
+    L.or_log2_fp32.restype = ctypes.c_float
+    L.or_log2_fp32.argtypes = [ctypes.c_float]
+    L.or_exp2_fp32.restype = ctypes.c_float
+    L.or_exp2_fp32.argtypes = [ctypes.c_float]
+    L.or_pow_fp32.restype = ctypes.c_float
+    L.or_pow_fp32.argtypes = [ctypes.c_float, ctypes.c_float]
+    L.or_optstate_quantize.argtypes = [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, ctypes.c_int]
+    L.or_optstate_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, ctypes.c_int]
     _lib = L
     return L
 
@@ -319,3 +327,44 @@ def gemm_entries(qa, sa, ta, fa, qb, sb, tb, fb, M, N, K, ii, jj, alpha=1.0, had
     if rc != 0:
         raise ValueError("oracle: bad gemm_entries arguments")
     return C, bound
+
+
+# ---------------------------------------------------------------- COAT optimizer states
+def log2_fp32(x):
+    return _load().or_log2_fp32(float(x))
+
+
+def exp2_fp32(y):
+    return _load().or_exp2_fp32(float(y))
+
+
+def pow_fp32(u, k):
+    return _load().or_pow_fp32(float(u), float(k))
+
+
+def optstate_quantize(x, fmt="e4m3", group=128, nthreads=None):
+    """[COAT, "解決方案：動態範圍擴充套件"]: FP8 codes of an fp32 optimizer state
+    after the per-group expansion u^k.  Returns (codes uint8 [n], amax
+    float32 [n/group], k float32 [n/group]) for the flattened x."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32).ravel())
+    n = x.size
+    q = np.zeros(n, np.uint8)
+    amax = np.zeros(n // group, np.float32)
+    k = np.zeros(n // group, np.float32)
+    rc = _load().or_optstate_quantize(_ptr(x), n, group, _fmt(fmt), _ptr(q), _ptr(amax), _ptr(k),
+                                      nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle: bad optimizer-state arguments")
+    return q, amax, k
+
+
+def optstate_dequantize(q, amax, k, fmt="e4m3", group=128, nthreads=None):
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8).ravel())
+    amax = np.ascontiguousarray(amax, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    out = np.zeros(q.size, np.float32)
+    rc = _load().or_optstate_dequantize(_ptr(q), _ptr(amax), _ptr(k), q.size, group, _fmt(fmt), _ptr(out),
+                                        nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle: bad optimizer-state arguments")
+    return out

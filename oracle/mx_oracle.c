@@ -646,3 +646,162 @@ int or_gemm_entries(const uint8_t* qa, const uint8_t* sa, const float* ta, int f
     parallel_for(n, nthreads, gemm_entries_range, &J);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* FP8 optimizer states with dynamic range expansion ([COAT, "解決方案：  */
+/* 動態範圍擴充套件"]).  The page states the goal -- an expansion function */
+/* applied before quantization, with one parameter k per quantization  */
+/* group computed on the fly, that stretches the group's max/min ratio */
+/* to the FP8 format's (about 2e5 for E4M3) -- but its formula did not */
+/* survive.  Reading, after the COAT paper the page cites: f(x) =      */
+/* sign(x)|x|^k.  Per group, with the magnitudes normalised by the     */
+/* group's largest one so that every power stays in fp32 range:        */
+/*   u = |x| / amax,  k = log2(R_fmt) / log2(amax / amin_nonzero),     */
+/*   y = sign(x) * u^k * Fmax  -> FP8 code (RNE, saturating),          */
+/* so the largest magnitude maps to Fmax and the smallest nonzero one  */
+/* to Fmax / R_fmt = the smallest subnormal; R_fmt = Fmax / (smallest  */
+/* subnormal).  Stored per group: amax and k.  Inverse:                */
+/*   x = sign(q) * amax * (|decode(q)| / Fmax)^(1/k).                  */
+/* The powers go through log2 and exp2.  So that the codes are a plain */
+/* function of fp32 arithmetic, both are written out as fixed fp32     */
+/* polynomial evaluations (every operation rounded once, in the order  */
+/* written): log2 from the atanh series in t = (m-1)/(m+1), exp2 from  */
+/* the Taylor series of e^(f ln 2) on [-1/2, 1/2].                     */
+/* ------------------------------------------------------------------ */
+float or_log2_fp32(float x)
+{
+    /* x > 0 finite.  x = m * 2^e with m in [sqrt(1/2), sqrt(2)) */
+    int e = 0;
+    if (x < 0x1p-126f) { x = x * 0x1p32f; e = -32; }          /* subnormal: exact scaling */
+    uint32_t b;
+    memcpy(&b, &x, 4);
+    e += (int)((b >> 23) & 0xFFu) - 127;
+    b = (b & 0x7FFFFFu) | 0x3F800000u;
+    float m;
+    memcpy(&m, &b, 4);
+    if (m > 1.41421356f) { m = m * 0.5f; e += 1; }
+    const float t = (m - 1.0f) / (m + 1.0f);
+    const float t2 = t * t;
+    /* 2/ln2 * (t + t^3/3 + ... + t^9/9) */
+    float p = 0.320598898f;
+    p = p * t2 + 0.412198583f;
+    p = p * t2 + 0.577078016f;
+    p = p * t2 + 0.961796694f;
+    p = p * t2 + 2.88539008f;
+    return (float)e + t * p;
+}
+
+float or_exp2_fp32(float y)
+{
+    if (y != y) return y;
+    if (y >= 128.0f) return INFINITY;
+    if (y < -150.0f) return 0.0f;
+    const float n = floorf(y + 0.5f);
+    const float z = (y - n) * 0.693147181f;                    /* f ln 2, |f| <= 1/2 */
+    float p = 1.98412698e-4f;                                  /* 1/5040 */
+    p = p * z + 1.38888889e-3f;                                /* 1/720 */
+    p = p * z + 8.33333377e-3f;                                /* 1/120 */
+    p = p * z + 4.16666679e-2f;                                /* 1/24 */
+    p = p * z + 0.166666672f;                                  /* 1/6 */
+    p = p * z + 0.5f;
+    p = p * z + 1.0f;
+    p = p * z + 1.0f;
+    return ldexpf(p, (int)n);
+}
+
+/* u^k for u >= 0 */
+float or_pow_fp32(float u, float k)
+{
+    if (u == 0.0f) return 0.0f;
+    return or_exp2_fp32(k * or_log2_fp32(u));
+}
+
+/* log2 of the format's dynamic range Fmax / smallest subnormal, as an fp32
+ * constant: E4M3 448 / 2^-9, E5M2 57344 / 2^-16 */
+static float log2_range(int fmt)
+{
+    return fmt == OR_E4M3 ? 17.8073549f : 31.8073549f;
+}
+
+typedef struct {
+    const float* x; int64_t group; int fmt;
+    uint8_t* q; float* amax; float* kexp;
+} os_job;
+
+static void os_quant_range(int64_t lo, int64_t hi, void* arg)
+{
+    const os_job* J = (const os_job*)arg;
+    const int64_t G = J->group;
+    const float fmax = (float)or_fmax(J->fmt);
+    for (int64_t g = lo; g < hi; g++) {
+        const float* x = J->x + g * G;
+        uint8_t* q = J->q + g * G;
+        int finite = 1;
+        float amax = 0.0f, amin = INFINITY;
+        for (int64_t i = 0; i < G; i++) {
+            const float a = fabsf(x[i]);
+            if (!isfinite(a)) finite = 0;
+            if (a > amax) amax = a;
+            if (a > 0.0f && a < amin) amin = a;
+        }
+        if (!finite) {
+            for (int64_t i = 0; i < G; i++) q[i] = 0x7F;
+            J->amax[g] = NAN;
+            J->kexp[g] = NAN;
+            continue;
+        }
+        if (amax == 0.0f) {                          /* all zero: signed zeros, unit parameters */
+            for (int64_t i = 0; i < G; i++) q[i] = signbit(x[i]) ? (uint8_t)0x80 : (uint8_t)0x00;
+            J->amax[g] = 1.0f;
+            J->kexp[g] = 1.0f;
+            continue;
+        }
+        const float r = amax / amin;
+        const float k = r > 1.0f ? log2_range(J->fmt) / or_log2_fp32(r) : 1.0f;
+        for (int64_t i = 0; i < G; i++) {
+            const float u = fabsf(x[i]) / amax;
+            float y = or_pow_fp32(u, k) * fmax;
+            if (signbit(x[i])) y = -y;
+            q[i] = (uint8_t)or_encode_rne(J->fmt, (double)y);
+        }
+        J->amax[g] = amax;
+        J->kexp[g] = k;
+    }
+}
+
+int or_optstate_quantize(const float* x, int64_t n, int64_t group, int fmt, uint8_t* q, float* amax,
+                         float* kexp, int nthreads)
+{
+    if (group <= 0 || n <= 0 || n % group != 0 || (fmt != OR_E4M3 && fmt != OR_E5M2)) return -1;
+    os_job J = {x, group, fmt, q, amax, kexp};
+    parallel_for(n / group, nthreads, os_quant_range, &J);
+    return 0;
+}
+
+static void os_dequant_range(int64_t lo, int64_t hi, void* arg)
+{
+    const os_job* J = (const os_job*)arg;              /* x is the output here */
+    const int64_t G = J->group;
+    const float fmax = (float)or_fmax(J->fmt);
+    float* out = (float*)J->x;
+    for (int64_t g = lo; g < hi; g++) {
+        const float amax = J->amax[g], k = J->kexp[g];
+        const float kinv = 1.0f / k;
+        for (int64_t i = 0; i < G; i++) {
+            const unsigned c = J->q[g * G + i];
+            const float v = (float)or_decode(J->fmt, c);
+            float a = amax * or_pow_fp32(fabsf(v) / fmax, kinv);
+            if (v != v || amax != amax || k != k) a = NAN;
+            out[g * G + i] = (c & 0x80u) ? -a : a;
+        }
+    }
+}
+
+int or_optstate_dequantize(const uint8_t* q, const float* amax, const float* kexp, int64_t n, int64_t group,
+                           int fmt, float* out, int nthreads)
+{
+    if (group <= 0 || n <= 0 || n % group != 0 || (fmt != OR_E4M3 && fmt != OR_E5M2)) return -1;
+    os_job J = {out, group, fmt, (uint8_t*)q, (float*)amax, (float*)kexp};
+    parallel_for(n / group, nthreads, os_dequant_range, &J);
+    return 0;
+}

@@ -104,6 +104,18 @@ int or_gemm_entries(const uint8_t* qa, const uint8_t* sa, const float* ta, int f
                     const int64_t* ii, const int64_t* jj, int64_t n,
                     double* C, double* bound, int nthreads);
 
+/* ---- FP8 optimizer states with dynamic range expansion [COAT] ----
+ * Groups of `group` consecutive fp32 values; per group amax and the
+ * expansion exponent k; codes one byte per element (E4M3 or E5M2).
+ * Returns 0, or -1 on bad arguments. */
+float or_log2_fp32(float x);                 /* fixed fp32 evaluation, x > 0 */
+float or_exp2_fp32(float y);
+float or_pow_fp32(float u, float k);         /* u^k, u >= 0 */
+int or_optstate_quantize(const float* x, int64_t n, int64_t group, int fmt, uint8_t* q, float* amax,
+                         float* kexp, int nthreads);
+int or_optstate_dequantize(const uint8_t* q, const float* amax, const float* kexp, int64_t n, int64_t group,
+                           int fmt, float* out, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
