@@ -204,6 +204,39 @@ def setup_autoscale(args):
     return step, info
 
 
+def setup_coat(args):
+    """COAT FP8 optimizer states: Adam's first and second moments of the
+    Llama-3-8B gate-up weight (4096 x 28672 fp32 each) held as E4M3 codes
+    with per-group (128) dynamic range expansion.  One step reads both
+    states back (dequantize) and stores them again (quantize) -- the
+    optimizer's read-modify-write of its states without the update
+    arithmetic."""
+    w = I.make("coat_optstate_llama_wgu")
+    G = 128
+    st = {}
+    for name in ("m", "v"):
+        x = torch.from_numpy(w.tensors[name].ravel()).cuda()
+        q, amax, k = mx.mx_quantize_optstate(x, "e4m3", G)
+        st[name] = (x, q, amax, k, torch.empty_like(x))
+
+    def step(t):
+        for name, (x, q, amax, k, out) in st.items():
+            t.run("dequant_" + name, lambda q=q, amax=amax, k=k, out=out: mx.mx_dequantize_optstate(
+                q, amax, k, "e4m3", G, out=out))
+            t.run("quant_" + name, lambda x=x, q=q, amax=amax, k=k: mx.mx_quantize_optstate(
+                x, "e4m3", G, q=q, amax=amax, kexp=k))
+
+    n = w.tensors["m"].size
+    # per element 4 bytes of fp32 and 1 code byte; 8 bytes of parameters per group
+    b = 4 * n + n + 8 * (n // G)
+    info = dict(flops=0.0, qbytes={f"{op}_{s_}": b for op in ("dequant", "quant") for s_ in ("m", "v")},
+                gemm_kernel=None, mfma=None,
+                config={"workload": "coat_fp8_optimizer_states_llama3_8b_wgu", "elements_per_state": n,
+                        "group": G, "elem": "e4m3 + e4m3", "states": "adam m, v (fp32)"},
+                host=w.tensors)
+    return step, info
+
+
 def setup_fp4(args):
     w = I.make("mxfp4_wgrad_qkv")
     dY = to_dev(w.tensors["dY"])          # [T][Q]
@@ -305,7 +338,7 @@ def setup_copy(args):
 
 
 WORKLOADS = {"moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4, "llama": setup_llama,
-             "copy": setup_copy, "autoscale": setup_autoscale, "mxout": setup_mxout}
+             "copy": setup_copy, "autoscale": setup_autoscale, "mxout": setup_mxout, "coat": setup_coat}
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -481,7 +514,8 @@ def main():
                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic(args.workload),
                     "kernel": {"dual": "k_quant_tile_dma (dual layout)",
-                               "autoscale": "k_amax_partial x2 + k_predict_scale"}.get(args.workload, n)}
+                               "autoscale": "k_amax_partial x2 + k_predict_scale",
+                               "coat": "k_optstate_dequant (first moment)"}.get(args.workload, n)}
         value = gbs
         metric = "mx_quantize GB/s (% HBM peak)"
         unit = "GB/s"

@@ -180,6 +180,52 @@ mx_status mx_predict_tensor_scale_noalloc(const void* w, int64_t ld_w, const voi
 
 namespace {
 
+mx_status check_optstate(int64_t n, int32_t group, int32_t fmt)
+{
+    if (fmt == MX_E2M1) return fail(MX_ERR_UNSUPPORTED, "optimizer states are quantized to FP8 (E4M3 or E5M2)");
+    if (fmt != MX_E4M3 && fmt != MX_E5M2) return fail(MX_ERR_INVALID_ARG, "unknown element format");
+    if (group != 32 && group != 64 && group != 128 && group != 256)
+        return fail(MX_ERR_INVALID_ARG, "group must be 32, 64, 128 or 256");
+    if (n <= 0 || n % group != 0) return fail(MX_ERR_INVALID_ARG, "n must be a positive multiple of group");
+    return MX_OK;
+}
+
+}  // namespace
+
+mx_status mx_quantize_optstate(const float* x, int64_t n, int32_t group, int32_t fmt, uint8_t* q, float* amax,
+                               float* kexp, void* stream)
+{
+    g_msg[0] = '\0';
+    if (!x || !q || !amax || !kexp) return fail(MX_ERR_INVALID_ARG, "x, q, amax and kexp must not be NULL");
+    mx_status s = check_optstate(n, group, fmt);
+    if (s != MX_OK) return s;
+    if (!aligned16(x)) return fail(MX_ERR_ALIGNMENT, "x must be 16-byte aligned");
+    if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(amax) | reinterpret_cast<uintptr_t>(kexp)) & 3u) != 0)
+        return fail(MX_ERR_ALIGNMENT, "q, amax and kexp must be 4-byte aligned");
+    mx::OptStateJob j{};
+    j.x = x; j.n = n; j.group = group; j.fmt = fmt; j.dequant = false;
+    j.q = q; j.amax = amax; j.k = kexp;
+    return hip_status(mx::launch_optstate(j, (hipStream_t)stream));
+}
+
+mx_status mx_dequantize_optstate(const uint8_t* q, const float* amax, const float* kexp, int64_t n, int32_t group,
+                                 int32_t fmt, float* out, void* stream)
+{
+    g_msg[0] = '\0';
+    if (!q || !amax || !kexp || !out) return fail(MX_ERR_INVALID_ARG, "q, amax, kexp and out must not be NULL");
+    mx_status s = check_optstate(n, group, fmt);
+    if (s != MX_OK) return s;
+    if (!aligned16(out)) return fail(MX_ERR_ALIGNMENT, "out must be 16-byte aligned");
+    if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(amax) | reinterpret_cast<uintptr_t>(kexp)) & 3u) != 0)
+        return fail(MX_ERR_ALIGNMENT, "q, amax and kexp must be 4-byte aligned");
+    mx::OptStateJob j{};
+    j.n = n; j.group = group; j.fmt = fmt; j.dequant = true;
+    j.q = (uint8_t*)q; j.amax = (float*)amax; j.k = (float*)kexp; j.out = out;
+    return hip_status(mx::launch_optstate(j, (hipStream_t)stream));
+}
+
+namespace {
+
 mx_status check_gemm_operands(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,
                               const void* qb, const uint8_t* sb, const float* tb, int32_t fb,
                               int64_t M, int64_t N, int64_t K, int32_t hadamard_k)

@@ -38,6 +38,15 @@ hipError_t launch_predict(const PredictJob& j, hipStream_t stream);
 // the same with the library's own per-device scratch in place of j.work
 hipError_t launch_predict_noalloc(PredictJob j, hipStream_t stream);
 
+// FP8 optimizer states with dynamic range expansion: quantize (x -> q,
+// amax, k) or dequantize (q, amax, k -> out); n elements, group size G
+struct OptStateJob {
+    const float* x; int64_t n; int group; int fmt; bool dequant;
+    uint8_t* q; float* amax; float* k; float* out;
+};
+
+hipError_t launch_optstate(const OptStateJob& j, hipStream_t stream);
+
 struct DequantJob {
     const uint8_t* q; const uint8_t* scales; const float* tensor_scale;
     int fmt; int64_t rows, cols; int axis; bool hadamard;

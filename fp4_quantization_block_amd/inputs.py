@@ -87,10 +87,13 @@ FULL_SHAPES = {
     # MOSS weight auto-scaling on the 4096x4096 weight of the two-level
     # workload: this step's weights and gradient, and the page's lr
     "moss_weight_autoscale_4096": {"K": 4096, "N": 4096},
+    # COAT optimizer states: Adam's first and second moments of the
+    # Llama-3-8B gate-up weight (4096 x 28672), fp32
+    "coat_optstate_llama_wgu": {"H": 4096, "F2": 28672},
 }
 WORKLOAD_SEEDS = {"mxfp8_gemm_256": 1, "moss_two_level_4096": 2, "llama3_8b_mlp": 3,
                   "mxfp4_wgrad_qkv": 4, "dual_layout_16384x14336": 5,
-                  "moss_weight_autoscale_4096": 6}
+                  "moss_weight_autoscale_4096": 6, "coat_optstate_llama_wgu": 7}
 
 
 def make(name: str, **shape_override) -> Workload:
@@ -128,6 +131,15 @@ def make(name: str, **shape_override) -> Workload:
         w.tensors["W"] = to_bf16_bits(normal(seed, 0, (K, N), std=0.02))     # like the MOSS weight B
         w.tensors["G"] = to_bf16_bits(normal(seed, 1, (K, N), std=1e-3))     # like the MLP gradients
         w.meta["lr"] = 1e-3
+    elif name == "coat_optstate_llama_wgu":
+        H, F2 = shp["H"], shp["F2"]
+        # first moment: signed, N(0, 1e-3) (max/min within a 128-group of
+        # order 1e3, the page's figure); second moment: positive,
+        # log-normal 1e-6 * exp(N(0, 0.5)) (max/min of order 10)
+        w.tensors["m"] = normal(seed, 0, (H, F2), std=1e-3)
+        g = _rng(seed, 1)
+        w.tensors["v"] = (np.exp(g.standard_normal(size=(H, F2), dtype=np.float32) * np.float32(0.5))
+                          * np.float32(1e-6)).astype(np.float32)
     else:
         raise KeyError(name)
     return w

@@ -27,7 +27,7 @@ FMTS = {"e4m3": MX_E4M3, "e5m2": MX_E5M2, "e2m1": MX_E2M1}
 EXPORTED = ("mx_quantize", "mx_quantize_dual_layout", "mx_gemm", "mx_dequantize",
             "mx_status_string", "mx_last_error_message",
             "mx_predict_tensor_scale", "mx_predict_workspace_bytes", "mx_gemm_quantized",
-            "mx_predict_tensor_scale_noalloc")
+            "mx_predict_tensor_scale_noalloc", "mx_quantize_optstate", "mx_dequantize_optstate")
 
 
 class MXError(RuntimeError):
@@ -77,6 +77,10 @@ def load() -> ctypes.CDLL:
     L.mx_predict_tensor_scale_noalloc.restype = _i32
     L.mx_predict_tensor_scale_noalloc.argtypes = [_vp, _i64, _vp, _i64, _i32, _i64, _i64, ctypes.c_float,
                                                   _i32, _vp, _vp]
+    L.mx_quantize_optstate.restype = _i32
+    L.mx_quantize_optstate.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]
+    L.mx_dequantize_optstate.restype = _i32
+    L.mx_dequantize_optstate.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]
     L.mx_predict_workspace_bytes.restype = _i64
     L.mx_predict_workspace_bytes.argtypes = []
     L.mx_status_string.restype = ctypes.c_char_p
@@ -250,4 +254,28 @@ def mx_dequantize(q, scales, tensor_scale, fmt, rows: int, cols: int, axis: int,
                           device=q.device)
     _check(load().mx_dequantize(_ptr(q), _ptr(scales), _ptr(tensor_scale), _fmt(fmt), rows, cols,
                                 axis, int(bool(hadamard)), _ptr(out), out_dtype, _stream(stream)))
+    return out
+
+
+def mx_quantize_optstate(x: torch.Tensor, fmt="e4m3", group: int = 128, q=None, amax=None, kexp=None,
+                         stream=None):
+    """FP8 codes of an fp32 optimizer state after the per-group dynamic
+    range expansion; returns (q uint8 [n], amax fp32 [n/group], k fp32 [n/group])."""
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 tensor")
+    n = x.numel()
+    dev = x.device
+    q = torch.empty(n, dtype=torch.uint8, device=dev) if q is None else q
+    amax = torch.empty(n // group, dtype=torch.float32, device=dev) if amax is None else amax
+    kexp = torch.empty(n // group, dtype=torch.float32, device=dev) if kexp is None else kexp
+    _check(load().mx_quantize_optstate(_ptr(x), n, group, _fmt(fmt), _ptr(q), _ptr(amax), _ptr(kexp),
+                                       _stream(stream)))
+    return q, amax, kexp
+
+
+def mx_dequantize_optstate(q, amax, kexp, fmt="e4m3", group: int = 128, out=None, stream=None) -> torch.Tensor:
+    n = q.numel()
+    out = torch.empty(n, dtype=torch.float32, device=q.device) if out is None else out
+    _check(load().mx_dequantize_optstate(_ptr(q), _ptr(amax), _ptr(kexp), n, group, _fmt(fmt), _ptr(out),
+                                         _stream(stream)))
     return out

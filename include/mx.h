@@ -264,6 +264,45 @@ mx_status mx_predict_tensor_scale_noalloc(const void* w, int64_t ld_w, const voi
                                           int32_t src_dtype, int64_t rows, int64_t cols, float lr,
                                           int32_t fmt, float* scale_out, void* stream);
 
+/*
+ * mx_quantize_optstate -- FP8 optimizer states with dynamic range expansion
+ * ([COAT, "解決方案：動態範圍擴充套件"]): each group of `group` consecutive
+ * values of an fp32 optimizer state (e.g. Adam's first or second moment) is
+ * expanded by f(x) = sign(x)|x|^k, with one k per group computed on the
+ * fly, so that the group's max/min ratio matches the FP8 format's (Fmax /
+ * smallest subnormal, about 2.3e5 for E4M3), then quantized.  Per group:
+ *   amax = max|x|,  amin = smallest nonzero |x|,
+ *   k = log2(Fmax / smallest subnormal) / log2(amax / amin)   (1 if amax == amin),
+ *   q = RNE_saturating(sign(x) * (|x| / amax)^k * Fmax),
+ * so the largest magnitude gets the format's top code and the smallest
+ * nonzero one its smallest subnormal.  The page does not print f; the
+ * COAT paper's form is used, normalised by amax (its per-group scale
+ * amax^k / Fmax is then implicit).  Powers are exp2(k * log2(u)) with log2
+ * and exp2 evaluated as a fixed sequence of fp32 operations (see
+ * optstate.hip), so the codes depend only on IEEE fp32 arithmetic.
+ * An all-zero group gets signed-zero codes, amax = k = 1; a group holding
+ * a NaN or Inf gets the NaN code 0x7F everywhere and amax = k = NaN.
+ *
+ * x:      n fp32 values (device), 16-byte aligned; groups are consecutive.
+ * n:      > 0, a multiple of group.
+ * group:  32, 64, 128 or 256.
+ * fmt:    MX_E4M3 or MX_E5M2 (MX_E2M1: MX_ERR_UNSUPPORTED).
+ * q:      n codes, one byte each, 4-byte aligned.
+ * amax, kexp: n / group fp32 each (the group's max |x| and k), 4-byte aligned.
+ * Errors: MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_ALIGNMENT, MX_ERR_HIP.
+ */
+mx_status mx_quantize_optstate(const float* x, int64_t n, int32_t group, int32_t fmt, uint8_t* q, float* amax,
+                               float* kexp, void* stream);
+
+/*
+ * mx_dequantize_optstate -- the inverse: out = sign(q) * amax *
+ * (|decode(q)| / Fmax)^(1/k), per element, with 1/k one fp32 division and
+ * the power as in mx_quantize_optstate; NaN where the code, amax or k is NaN.
+ * Arguments as mx_quantize_optstate; out: n fp32, 16-byte aligned.
+ */
+mx_status mx_dequantize_optstate(const uint8_t* q, const float* amax, const float* kexp, int64_t n, int32_t group,
+                                 int32_t fmt, float* out, void* stream);
+
 /* Static text for a status code. */
 const char* mx_status_string(mx_status status);
 
