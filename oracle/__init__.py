@@ -92,6 +92,11 @@ def _load():
     L.or_pow_fp32.argtypes = [ctypes.c_float, ctypes.c_float]
     L.or_optstate_quantize.argtypes = [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, ctypes.c_int]
     L.or_optstate_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, ctypes.c_int]
+    L.or_nvfp_quantize.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp,
+                                   ctypes.c_int]
+    L.or_nvfp_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
+    L.or_nvfp_gemm.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64,
+                               ctypes.c_double, _vp, _vp, ctypes.c_int]
     _lib = L
     return L
 
@@ -368,3 +373,55 @@ def optstate_dequantize(q, amax, k, fmt="e4m3", group=128, nthreads=None):
     if rc != 0:
         raise ValueError("oracle: bad optimizer-state arguments")
     return out
+
+
+# ---------------------------------------------------------------- nvfp routes
+NV_PANEL = 32
+
+
+def nvfp_shapes(rows, cols, axis, local):
+    """(codes shape, block-scale shape, tensor-scale count) of a stored nvfp copy."""
+    SR, L = (rows, cols) if axis == AXIS_ROW else (cols, rows)
+    return (SR, L // 2), (SR, L // 16), ((SR + NV_PANEL - 1) // NV_PANEL if local else 1)
+
+
+def nvfp_quantize(x, axis, local=False, nthreads=None):
+    """[FAF, "格式感知融合的设计思路"]: NVFP4 copy (E2M1, E4M3 scale per 16,
+    FP32 second-level scale global or per 32 stored rows).  Returns
+    (codes, block scales, second-level scales)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    qs, ss, nt = nvfp_shapes(rows, cols, axis, local)
+    q = np.zeros(qs, np.uint8)
+    s = np.zeros(ss, np.uint8)
+    t = np.zeros(nt, np.float32)
+    rc = _load().or_nvfp_quantize(_ptr(x), _src(x), rows, cols, cols, axis, int(bool(local)), _ptr(q), _ptr(s),
+                                  _ptr(t), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle: bad nvfp shape")
+    return q, s, t
+
+
+def nvfp_dequantize(q, s16, tscale, rows, cols, axis, local=False):
+    q = np.ascontiguousarray(q, np.uint8)
+    s16 = np.ascontiguousarray(s16, np.uint8)
+    t = np.ascontiguousarray(tscale, np.float32)
+    out = np.zeros((rows, cols), np.float32)
+    rc = _load().or_nvfp_dequantize(_ptr(q), _ptr(s16), _ptr(t), rows, cols, axis, int(bool(local)), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle: bad nvfp shape")
+    return out
+
+
+def nvfp_gemm(qa, sa, ta, local_a, qb, sb, tb, local_b, M, N, K, alpha=1.0, nthreads=None):
+    """C[M][N] (float64) and the bound |alpha'| (|A|.|B|) of the nvfp GEMM."""
+    qa, sa, qb, sb = (np.ascontiguousarray(a, np.uint8) for a in (qa, sa, qb, sb))
+    ta, tb = np.ascontiguousarray(ta, np.float32), np.ascontiguousarray(tb, np.float32)
+    C = np.zeros((M, N))
+    bound = np.zeros((M, N))
+    rc = _load().or_nvfp_gemm(_ptr(qa), _ptr(sa), _ptr(ta), int(bool(local_a)), _ptr(qb), _ptr(sb), _ptr(tb),
+                              int(bool(local_b)), M, N, K, float(alpha), _ptr(C), _ptr(bound),
+                              nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle: bad nvfp gemm arguments")
+    return C, bound

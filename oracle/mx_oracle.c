@@ -805,3 +805,167 @@ int or_optstate_dequantize(const uint8_t* q, const float* amax, const float* kex
     parallel_for(n / group, nthreads, os_dequant_range, &J);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* nvfp routes ([FAF, "格式感知融合的设计思路"]: native mxfp, global nvfp  */
+/* and CTA-local nvfp, each quantization producer bound to its scale  */
+/* domain and consumer layout; [FAF, "FP4加速为何常常纸上富贵"]: nvfp is  */
+/* block scaling, one scale per block of values).  The pages fix       */
+/* neither block size nor scale format; reading: NVIDIA's published    */
+/* NVFP4 -- E2M1 elements in blocks of 16 along the stored row, an     */
+/* unsigned E4M3 scale per block, and an FP32 second-level scale       */
+/* s = amax / (6 * 448) so that every block scale fits E4M3:           */
+/*   global: one s over the tensor;                                    */
+/*   local:  one s per panel of 32 stored rows (the rows one GEMM tile  */
+/*           consumes over all of K), no reduction across panels.      */
+/* Per block: den = RN(6 s); sb = E4M3_RNE_sat(RN(amax_b / den));       */
+/* d = RN(decode(sb) * s); r = RN(1 / d); code_i = E2M1_RNE_sat(RN(v_i * */
+/* r)).  A zero block scale gives signed zeros; a block holding a NaN  */
+/* or Inf gets scale code 0x7F (E4M3 NaN) and zero codes.              */
+/* ------------------------------------------------------------------ */
+#define NV_PANEL 32
+
+typedef struct {
+    const void* x; int src; int64_t rows, cols, ld; int axis, local;
+    uint8_t* q; uint8_t* s16; const float* ts;
+} nv_job;
+
+/* element (stored row sr, position c along it) of the source */
+static float nv_src(const nv_job* J, int64_t sr, int64_t c)
+{
+    return J->axis == OR_AXIS_ROW ? load_src(J->x, J->src, sr * J->ld + c)
+                                  : load_src(J->x, J->src, c * J->ld + sr);
+}
+
+static void nv_quant_range(int64_t lo, int64_t hi, void* arg)
+{
+    const nv_job* J = (const nv_job*)arg;
+    const int64_t L = J->axis == OR_AXIS_ROW ? J->cols : J->rows;       /* stored row length */
+    const int64_t nb = L / 16;
+    for (int64_t sr = lo; sr < hi; sr++) {
+        const float s = J->ts[J->local ? sr / NV_PANEL : 0];
+        for (int64_t b = 0; b < nb; b++) {
+            float v[16];
+            float amax = 0.0f;
+            int finite = 1;
+            for (int i = 0; i < 16; i++) {
+                v[i] = nv_src(J, sr, b * 16 + i);
+                if (!isfinite(v[i])) finite = 0;
+                if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+            }
+            unsigned sb;
+            unsigned codes[16];
+            if (!finite || s != s) {
+                sb = 0x7F;
+                for (int i = 0; i < 16; i++) codes[i] = 0;
+            } else {
+                const float den = 6.0f * s;
+                sb = or_encode_rne(OR_E4M3, (double)(amax / den)) & 0x7Fu;   /* unsigned scale */
+                const float ds = (float)or_decode(OR_E4M3, sb);
+                if (ds == 0.0f) {
+                    for (int i = 0; i < 16; i++) codes[i] = signbit(v[i]) ? 0x8u : 0x0u;
+                } else {
+                    const float d = ds * s;
+                    const float r = 1.0f / d;
+                    for (int i = 0; i < 16; i++) codes[i] = or_encode_rne(OR_E2M1, (double)(v[i] * r));
+                }
+            }
+            J->s16[sr * nb + b] = (uint8_t)sb;
+            for (int i = 0; i < 16; i++) put_code(J->q, 4, L / 2, sr, b * 16 + i, codes[i]);
+        }
+    }
+}
+
+/* second-level scale of one domain: amax / (6 * 448), 1 for an all-zero
+ * domain, NaN when it holds a NaN or Inf */
+static float nv_domain_scale(const nv_job* J, int64_t sr0, int64_t sr1)
+{
+    const int64_t L = J->axis == OR_AXIS_ROW ? J->cols : J->rows;
+    float amax = 0.0f;
+    for (int64_t sr = sr0; sr < sr1; sr++)
+        for (int64_t c = 0; c < L; c++) {
+            const float a = fabsf(nv_src(J, sr, c));
+            if (!isfinite(a)) return NAN;
+            if (a > amax) amax = a;
+        }
+    return amax == 0.0f ? 1.0f : amax / 2688.0f;
+}
+
+int or_nvfp_quantize(const void* x, int src, int64_t rows, int64_t cols, int64_t ld, int axis, int local,
+                     uint8_t* q, uint8_t* s16, float* tscale, int nthreads)
+{
+    const int64_t SR = axis == OR_AXIS_ROW ? rows : cols, L = axis == OR_AXIS_ROW ? cols : rows;
+    if (rows <= 0 || cols <= 0 || ld < cols || L % 16 != 0) return -1;
+    nv_job J = {x, src, rows, cols, ld, axis, local, q, s16, tscale};
+    if (local) {
+        for (int64_t p = 0; p * NV_PANEL < SR; p++)
+            tscale[p] = nv_domain_scale(&J, p * NV_PANEL, (p + 1) * NV_PANEL < SR ? (p + 1) * NV_PANEL : SR);
+    } else {
+        tscale[0] = nv_domain_scale(&J, 0, SR);
+    }
+    parallel_for(SR, nthreads, nv_quant_range, &J);
+    return 0;
+}
+
+/* x_hat = RN(RN(decode(code) * decode(sb)) * s): the first product is exact
+ * (at most 6 significant bits), the second rounds once */
+int or_nvfp_dequantize(const uint8_t* q, const uint8_t* s16, const float* tscale, int64_t rows, int64_t cols,
+                       int axis, int local, float* out)
+{
+    const int64_t SR = axis == OR_AXIS_ROW ? rows : cols, L = axis == OR_AXIS_ROW ? cols : rows;
+    if (rows <= 0 || cols <= 0 || L % 16 != 0) return -1;
+    for (int64_t sr = 0; sr < SR; sr++) {
+        const float s = tscale[local ? sr / NV_PANEL : 0];
+        for (int64_t c = 0; c < L; c++) {
+            const float ds = (float)or_decode(OR_E4M3, s16[sr * (L / 16) + c / 16]);
+            const float e = (float)or_decode(OR_E2M1, get_code(q, 4, L / 2, sr, c));
+            const float v = (e * ds) * s;
+            if (axis == OR_AXIS_ROW) out[sr * cols + c] = v;
+            else out[c * cols + sr] = v;
+        }
+    }
+    return 0;
+}
+
+typedef struct {
+    const uint8_t *qa, *sa, *qb, *sb; const float *ta, *tb; int la, lb;
+    int64_t N, K; double alpha; double *C, *bound;
+} nvg_job;
+
+static double nv_elem(const uint8_t* q, const uint8_t* s, int64_t K, int64_t row, int64_t k)
+{
+    return or_decode(OR_E2M1, get_code(q, 4, K / 2, row, k)) * or_decode(OR_E4M3, s[row * (K / 16) + k / 16]);
+}
+
+static void nvg_range(int64_t lo, int64_t hi, void* arg)
+{
+    const nvg_job* J = (const nvg_job*)arg;
+    for (int64_t i = lo; i < hi; i++) {
+        const double sA = J->ta[J->la ? i / NV_PANEL : 0];
+        for (int64_t j = 0; j < J->N; j++) {
+            const double sB = J->tb[J->lb ? j / NV_PANEL : 0];
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < J->K; k++) {
+                const double a = nv_elem(J->qa, J->sa, J->K, i, k), b = nv_elem(J->qb, J->sb, J->K, j, k);
+                acc += a * b;
+                mag += fabs(a * b);
+            }
+            const double ap = J->alpha * sA * sB;
+            J->C[i * J->N + j] = ap * acc;
+            J->bound[i * J->N + j] = fabs(ap) * mag;
+        }
+    }
+}
+
+/* C[i][j] = alpha * sA(i) * sB(j) * sum_k Ahat[i][k] Bhat[j][k] in double, with
+ * Ahat = decode(code) * decode(block scale) (exact) and sA(i) the second-level
+ * scale of row i's domain (one, or one per 32-row panel); bound as or_gemm. */
+int or_nvfp_gemm(const uint8_t* qa, const uint8_t* sa, const float* ta, int local_a,
+                 const uint8_t* qb, const uint8_t* sb, const float* tb, int local_b,
+                 int64_t M, int64_t N, int64_t K, double alpha, double* C, double* bound, int nthreads)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return -1;
+    nvg_job J = {qa, sa, qb, sb, ta, tb, local_a, local_b, N, K, alpha, C, bound};
+    parallel_for(M, nthreads, nvg_range, &J);
+    return 0;
+}

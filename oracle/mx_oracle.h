@@ -116,6 +116,19 @@ int or_optstate_quantize(const float* x, int64_t n, int64_t group, int fmt, uint
 int or_optstate_dequantize(const uint8_t* q, const float* amax, const float* kexp, int64_t n, int64_t group,
                            int fmt, float* out, int nthreads);
 
+/* ---- nvfp routes [FAF] (reading: NVFP4, blocks of 16, E4M3 scales) ----
+ * local = 0: one FP32 second-level scale (global); 1: one per 32 stored
+ * rows.  Copies stored as mx: axis ROW [rows][cols/2] bytes, COL
+ * [cols][rows/2]; block scales [stored rows][row length / 16]; tscale
+ * [1] or [ceil(stored rows / 32)].  Returns 0, or -1 on bad shapes. */
+int or_nvfp_quantize(const void* x, int src, int64_t rows, int64_t cols, int64_t ld, int axis, int local,
+                     uint8_t* q, uint8_t* s16, float* tscale, int nthreads);
+int or_nvfp_dequantize(const uint8_t* q, const uint8_t* s16, const float* tscale, int64_t rows, int64_t cols,
+                       int axis, int local, float* out);
+int or_nvfp_gemm(const uint8_t* qa, const uint8_t* sa, const float* ta, int local_a,
+                 const uint8_t* qb, const uint8_t* sb, const float* tb, int local_b,
+                 int64_t M, int64_t N, int64_t K, double alpha, double* C, double* bound, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
