@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmx.so")
-SOURCES = ["abi.cpp", "quant.hip", "dequant.hip", "gemm.hip", "optstate.hip"]
+SOURCES = ["abi.cpp", "quant.hip", "dequant.hip", "gemm.hip", "optstate.hip", "nvfp.hip"]
 ARCH = os.environ.get("MX_OFFLOAD_ARCH", "gfx950")
 
 

@@ -226,6 +226,93 @@ mx_status mx_dequantize_optstate(const uint8_t* q, const float* amax, const floa
 
 namespace {
 
+// stored rows and their length of one nvfp copy
+void nv_dims(int64_t rows, int64_t cols, int32_t axis, int64_t* SR, int64_t* L)
+{
+    *SR = axis == MX_AXIS_ROW ? rows : cols;
+    *L = axis == MX_AXIS_ROW ? cols : rows;
+}
+
+mx_status check_nv_copy(int64_t rows, int64_t cols, int32_t axis, int32_t local)
+{
+    if (axis != MX_AXIS_ROW && axis != MX_AXIS_COL) return fail(MX_ERR_INVALID_ARG, "unknown axis");
+    if (local != 0 && local != 1) return fail(MX_ERR_INVALID_ARG, "local must be 0 or 1");
+    if (rows <= 0 || cols <= 0) return fail(MX_ERR_INVALID_ARG, "rows and cols must be > 0");
+    int64_t SR, L;
+    nv_dims(rows, cols, axis, &SR, &L);
+    if (L % 16 != 0) return fail(MX_ERR_INVALID_ARG, "the blocked dimension must be a multiple of 16");
+    return MX_OK;
+}
+
+}  // namespace
+
+mx_status mx_quantize_nvfp(const void* x, int32_t src_dtype, int64_t rows, int64_t cols, int64_t ld,
+                           int32_t axis, int32_t local, uint8_t* q, uint8_t* scales, float* tscale,
+                           void* stream)
+{
+    g_msg[0] = '\0';
+    mx_status s = check_source(x, src_dtype, rows, cols, ld);
+    if (s != MX_OK) return s;
+    if ((s = check_nv_copy(rows, cols, axis, local)) != MX_OK) return s;
+    if (!q || !scales || !tscale) return fail(MX_ERR_INVALID_ARG, "q, scales and tscale must not be NULL");
+    if (!aligned16(q)) return fail(MX_ERR_ALIGNMENT, "q must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(tscale) & 3u) return fail(MX_ERR_ALIGNMENT, "tscale must be 4-byte aligned");
+    mx::NvQuantJob j{};
+    j.x = x; j.src = src_dtype; j.rows = rows; j.cols = cols; j.ld = ld; j.axis = axis; j.local = local;
+    j.q = q; j.s16 = scales; j.ts = tscale;
+    return hip_status(mx::launch_nv_quantize(j, (hipStream_t)stream));
+}
+
+mx_status mx_dequantize_nvfp(const uint8_t* q, const uint8_t* scales, const float* tscale, int64_t rows,
+                             int64_t cols, int32_t axis, int32_t local, void* out, int32_t out_dtype,
+                             void* stream)
+{
+    g_msg[0] = '\0';
+    mx_status s = check_nv_copy(rows, cols, axis, local);
+    if (s != MX_OK) return s;
+    if (!q || !scales || !tscale || !out) return fail(MX_ERR_INVALID_ARG, "q, scales, tscale and out must not be NULL");
+    if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return fail(MX_ERR_INVALID_ARG, "unknown output dtype");
+    if (!aligned16(q)) return fail(MX_ERR_ALIGNMENT, "q must be 16-byte aligned");
+    const uintptr_t es = out_dtype == MX_OUT_F32 ? 4 : 2;
+    if (reinterpret_cast<uintptr_t>(out) % es != 0) return fail(MX_ERR_ALIGNMENT, "out must be aligned to its element size");
+    if (reinterpret_cast<uintptr_t>(tscale) & 3u) return fail(MX_ERR_ALIGNMENT, "tscale must be 4-byte aligned");
+    mx::NvQuantJob j{};
+    j.rows = rows; j.cols = cols; j.axis = axis; j.local = local;
+    j.q = (uint8_t*)q; j.s16 = (uint8_t*)scales; j.ts = (float*)tscale;
+    return hip_status(mx::launch_nv_dequantize(j, out, out_dtype, (hipStream_t)stream));
+}
+
+mx_status mx_gemm_nvfp(const uint8_t* qa, const uint8_t* sa, const float* ta, int32_t local_a,
+                       const uint8_t* qb, const uint8_t* sb, const float* tb, int32_t local_b,
+                       int64_t M, int64_t N, int64_t K, float alpha, void* c, int32_t out_dtype,
+                       int64_t ldc, void* stream)
+{
+    g_msg[0] = '\0';
+    if (!qa || !sa || !ta || !qb || !sb || !tb || !c) return fail(MX_ERR_INVALID_ARG, "an operand pointer is NULL");
+    if ((local_a != 0 && local_a != 1) || (local_b != 0 && local_b != 1))
+        return fail(MX_ERR_INVALID_ARG, "local_a and local_b must be 0 or 1");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(MX_ERR_INVALID_ARG, "M, N, K must be > 0");
+    if (K % 64 != 0) return fail(MX_ERR_INVALID_ARG, "K must be a multiple of 64");
+    if (K > (int64_t)1 << 24) return fail(MX_ERR_INVALID_ARG, "K must be <= 2^24");
+    if (M > ((int64_t)1 << 31) - 256 || N > ((int64_t)1 << 31) - 256) return fail(MX_ERR_INVALID_ARG, "M and N must be < 2^31 - 256");
+    if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return fail(MX_ERR_INVALID_ARG, "unknown output dtype");
+    if (ldc < N) return fail(MX_ERR_INVALID_ARG, "ldc must be >= N");
+    if (!aligned16(qa) || !aligned16(qb)) return fail(MX_ERR_ALIGNMENT, "qa and qb must be 16-byte aligned");
+    if (((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sb) | reinterpret_cast<uintptr_t>(ta) |
+          reinterpret_cast<uintptr_t>(tb)) & 3u) != 0)
+        return fail(MX_ERR_ALIGNMENT, "sa, sb, ta and tb must be 4-byte aligned");
+    const uintptr_t es = out_dtype == MX_OUT_F32 ? 4 : 2;
+    if ((reinterpret_cast<uintptr_t>(c) % es) != 0) return fail(MX_ERR_ALIGNMENT, "c must be aligned to its element size");
+    mx::NvGemmJob j{};
+    j.qa = qa; j.sa = sa; j.ta = ta; j.la = local_a;
+    j.qb = qb; j.sb = sb; j.tb = tb; j.lb = local_b;
+    j.M = M; j.N = N; j.K = K; j.alpha = alpha;
+    j.c = c; j.out_dtype = out_dtype; j.ldc = ldc;
+    return hip_status(mx::launch_nv_gemm(j, (hipStream_t)stream));
+}
+
+namespace {
+
 mx_status check_gemm_operands(const void* qa, const uint8_t* sa, const float* ta, int32_t fa,
                               const void* qb, const uint8_t* sb, const float* tb, int32_t fb,
                               int64_t M, int64_t N, int64_t K, int32_t hadamard_k)

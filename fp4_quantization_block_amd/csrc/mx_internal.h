@@ -47,6 +47,25 @@ struct OptStateJob {
 
 hipError_t launch_optstate(const OptStateJob& j, hipStream_t stream);
 
+// nvfp routes: NVFP4 copies (E2M1, E4M3 scale per 16, FP32 second-level
+// scale over the tensor or per 32 stored rows)
+struct NvQuantJob {
+    const void* x; int src; int64_t rows, cols, ld; int axis; int local;
+    uint8_t* q; uint8_t* s16; float* ts;
+};
+
+hipError_t launch_nv_quantize(const NvQuantJob& j, hipStream_t stream);
+hipError_t launch_nv_dequantize(const NvQuantJob& j, const void* out, int out_dtype, hipStream_t stream);
+
+struct NvGemmJob {
+    const uint8_t* qa; const uint8_t* sa; const float* ta; int la;
+    const uint8_t* qb; const uint8_t* sb; const float* tb; int lb;
+    int64_t M, N, K; float alpha;
+    void* c; int out_dtype; int64_t ldc;
+};
+
+hipError_t launch_nv_gemm(const NvGemmJob& j, hipStream_t stream);
+
 struct DequantJob {
     const uint8_t* q; const uint8_t* scales; const float* tensor_scale;
     int fmt; int64_t rows, cols; int axis; bool hadamard;

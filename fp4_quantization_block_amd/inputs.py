@@ -90,10 +90,12 @@ FULL_SHAPES = {
     # COAT optimizer states: Adam's first and second moments of the
     # Llama-3-8B gate-up weight (4096 x 28672), fp32
     "coat_optstate_llama_wgu": {"H": 4096, "F2": 28672},
+    "nvfp_llama3_8b_gate": {"T": 8192, "H": 4096, "F": 14336},
 }
 WORKLOAD_SEEDS = {"mxfp8_gemm_256": 1, "moss_two_level_4096": 2, "llama3_8b_mlp": 3,
                   "mxfp4_wgrad_qkv": 4, "dual_layout_16384x14336": 5,
-                  "moss_weight_autoscale_4096": 6, "coat_optstate_llama_wgu": 7}
+                  "moss_weight_autoscale_4096": 6, "coat_optstate_llama_wgu": 7,
+                  "nvfp_llama3_8b_gate": 8}
 
 
 def make(name: str, **shape_override) -> Workload:
@@ -131,6 +133,12 @@ def make(name: str, **shape_override) -> Workload:
         w.tensors["W"] = to_bf16_bits(normal(seed, 0, (K, N), std=0.02))     # like the MOSS weight B
         w.tensors["G"] = to_bf16_bits(normal(seed, 1, (K, N), std=1e-3))     # like the MLP gradients
         w.meta["lr"] = 1e-3
+    elif name == "nvfp_llama3_8b_gate":
+        # Llama-3-8B gate projection, forward: activations with outlier
+        # channels (as the MOSS workload), weights N(0, 0.02^2); Y = X W
+        T, H, F = shp["T"], shp["H"], shp["F"]
+        w.tensors["X"] = to_bf16_bits(student_t_with_outlier_channels(seed, 0, (T, H)))
+        w.tensors["W"] = to_bf16_bits(normal(seed, 1, (H, F), std=0.02))
     elif name == "coat_optstate_llama_wgu":
         H, F2 = shp["H"], shp["F2"]
         # first moment: signed, N(0, 1e-3) (max/min within a 128-group of

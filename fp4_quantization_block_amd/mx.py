@@ -27,7 +27,9 @@ FMTS = {"e4m3": MX_E4M3, "e5m2": MX_E5M2, "e2m1": MX_E2M1}
 EXPORTED = ("mx_quantize", "mx_quantize_dual_layout", "mx_gemm", "mx_dequantize",
             "mx_status_string", "mx_last_error_message",
             "mx_predict_tensor_scale", "mx_predict_workspace_bytes", "mx_gemm_quantized",
-            "mx_predict_tensor_scale_noalloc", "mx_quantize_optstate", "mx_dequantize_optstate")
+            "mx_predict_tensor_scale_noalloc", "mx_quantize_optstate", "mx_dequantize_optstate",
+            "mx_quantize_nvfp", "mx_dequantize_nvfp", "mx_gemm_nvfp")
+NV_PANEL = 32                      # stored rows per CTA-local nvfp scale domain
 
 
 class MXError(RuntimeError):
@@ -81,6 +83,13 @@ def load() -> ctypes.CDLL:
     L.mx_quantize_optstate.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]
     L.mx_dequantize_optstate.restype = _i32
     L.mx_dequantize_optstate.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]
+    L.mx_quantize_nvfp.restype = _i32
+    L.mx_quantize_nvfp.argtypes = [_vp, _i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]
+    L.mx_dequantize_nvfp.restype = _i32
+    L.mx_dequantize_nvfp.argtypes = [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _i32, _vp]
+    L.mx_gemm_nvfp.restype = _i32
+    L.mx_gemm_nvfp.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i64, _i64, _i64, ctypes.c_float,
+                               _vp, _i32, _i64, _vp]
     L.mx_predict_workspace_bytes.restype = _i64
     L.mx_predict_workspace_bytes.argtypes = []
     L.mx_status_string.restype = ctypes.c_char_p
@@ -279,3 +288,46 @@ def mx_dequantize_optstate(q, amax, kexp, fmt="e4m3", group: int = 128, out=None
     _check(load().mx_dequantize_optstate(_ptr(q), _ptr(amax), _ptr(kexp), n, group, _fmt(fmt), _ptr(out),
                                          _stream(stream)))
     return out
+
+
+def nvfp_shapes(rows: int, cols: int, axis: int, local: bool):
+    """(codes, block scales, second-level scales) shapes of an nvfp copy."""
+    SR, L = (rows, cols) if axis == MX_AXIS_ROW else (cols, rows)
+    return (SR, L // 2), (SR, L // 16), ((SR + NV_PANEL - 1) // NV_PANEL if local else 1,)
+
+
+def mx_quantize_nvfp(x: torch.Tensor, axis: int = MX_AXIS_ROW, local: bool = False, q=None, scales=None,
+                     tscale=None, stream=None):
+    """NVFP4 copy of x with a global (local=False) or per-32-row-panel
+    (local=True) second-level scale; returns (q, scales, tscale)."""
+    src = _src(x)
+    rows, cols = x.shape
+    qs, ss, ts = nvfp_shapes(rows, cols, axis, local)
+    dev = x.device
+    q = torch.empty(qs, dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty(ss, dtype=torch.uint8, device=dev) if scales is None else scales
+    tscale = torch.empty(ts, dtype=torch.float32, device=dev) if tscale is None else tscale
+    _check(load().mx_quantize_nvfp(_ptr(x), src, rows, cols, x.stride(0), axis, int(bool(local)), _ptr(q),
+                                   _ptr(scales), _ptr(tscale), _stream(stream)))
+    return q, scales, tscale
+
+
+def mx_dequantize_nvfp(q, scales, tscale, rows: int, cols: int, axis: int = MX_AXIS_ROW, local: bool = False,
+                       out_dtype: int = MX_OUT_F32, out=None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32 if out_dtype == MX_OUT_F32 else torch.bfloat16,
+                          device=q.device)
+    _check(load().mx_dequantize_nvfp(_ptr(q), _ptr(scales), _ptr(tscale), rows, cols, axis, int(bool(local)),
+                                     _ptr(out), out_dtype, _stream(stream)))
+    return out
+
+
+def mx_gemm_nvfp(qa, sa, ta, local_a: bool, qb, sb, tb, local_b: bool, M: int, N: int, K: int,
+                 alpha: float = 1.0, out_dtype: int = MX_OUT_BF16, c=None, ldc=None, stream=None) -> torch.Tensor:
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.float32 if out_dtype == MX_OUT_F32 else torch.bfloat16,
+                        device=qa.device)
+    ldc = c.stride(0) if ldc is None else ldc
+    _check(load().mx_gemm_nvfp(_ptr(qa), _ptr(sa), _ptr(ta), int(bool(local_a)), _ptr(qb), _ptr(sb), _ptr(tb),
+                               int(bool(local_b)), M, N, K, float(alpha), _ptr(c), out_dtype, ldc, _stream(stream)))
+    return c

@@ -303,6 +303,76 @@ mx_status mx_quantize_optstate(const float* x, int64_t n, int32_t group, int32_t
 mx_status mx_dequantize_optstate(const uint8_t* q, const float* amax, const float* kexp, int64_t n, int32_t group,
                                  int32_t fmt, float* out, void* stream);
 
+/*
+ * mx_quantize_nvfp -- an NVFP4 copy of a matrix with its scale domain, for
+ * the nvfp routes of [FAF, "格式感知融合的设计思路"] (each quantization
+ * producer bound to its scale domain and its consumer's layout: global nvfp
+ * and CTA-local nvfp beside native mxfp) and [FAF, "FP4加速为何常常纸上富贵"]
+ * (nvfp: one scale per block).  The pages fix neither block size nor scale
+ * format; NVIDIA's NVFP4 is used: E2M1 codes in blocks of 16 along the
+ * stored row, an unsigned E4M3 scale per block, and an FP32 second-level
+ * scale s = amax / (6 * 448) over the scale domain:
+ *   local = 0 (global nvfp): one domain, the whole matrix (tscale[0]);
+ *   local = 1 (CTA-local nvfp): one domain per panel of 32 stored rows
+ *     (tscale[p] covers stored rows 32p .. 32p + 31), the rows one GEMM
+ *     tile consumes, so no reduction crosses panels.
+ * Per block of 16 (each step one fp32 rounding): den = 6 * s;
+ * sb = E4M3_RNE_saturating(block amax / den); d = decode(sb) * s;
+ * code_i = E2M1_RNE_saturating(x_i * (1 / d)).  s is 1 for an all-zero
+ * domain, NaN for one holding a NaN or Inf; a zero block scale gives
+ * signed-zero codes; a block holding a NaN or Inf, or in a NaN domain,
+ * gets scale code 0x7F (E4M3 NaN) and zero codes.
+ *
+ * x, src_dtype, rows, cols, ld: as mx_quantize (row-major source).
+ * axis:   MX_AXIS_ROW: stored rows are source rows (blocks along cols);
+ *         MX_AXIS_COL: stored rows are source columns (the transposed
+ *         copy, blocks along rows).  The blocked length L (cols or rows)
+ *         must be a multiple of 16; SR is the other dimension.
+ * q:      SR x L/2 bytes (two codes per byte, element 2j in the low
+ *         nibble), 16-byte aligned.
+ * scales: SR x L/16 E4M3 codes.
+ * tscale: 1 fp32 (global) or ceil(SR / 32) fp32 (local), 4-byte aligned.
+ * The global route runs three kernels (panel maxima, their reduction,
+ * quantization) and uses q as its scratch between them; the local route
+ * runs two.  Errors: MX_ERR_INVALID_ARG, MX_ERR_ALIGNMENT, MX_ERR_HIP.
+ */
+mx_status mx_quantize_nvfp(const void* x, int32_t src_dtype, int64_t rows, int64_t cols, int64_t ld,
+                           int32_t axis, int32_t local, uint8_t* q, uint8_t* scales, float* tscale,
+                           void* stream);
+
+/*
+ * mx_dequantize_nvfp -- out = RN(RN(e2m1(code) * e4m3(sb)) * s) per element
+ * (the first product exact), written row-major [rows][cols] (leading
+ * dimension cols) whichever axis the copy has.  Arguments as
+ * mx_quantize_nvfp; out: fp32 (MX_OUT_F32) or bf16 (MX_OUT_BF16, round to
+ * nearest even), aligned to its element size.
+ */
+mx_status mx_dequantize_nvfp(const uint8_t* q, const uint8_t* scales, const float* tscale, int64_t rows,
+                             int64_t cols, int32_t axis, int32_t local, void* out, int32_t out_dtype,
+                             void* stream);
+
+/*
+ * mx_gemm_nvfp -- the GEMM that consumes nvfp copies ([FAF,
+ * "格式感知融合的设计思路"]: the consumer applies each producer's scale
+ * domain):  C[i][j] = alpha * sA(i) * sB(j) * sum_k Ahat[i][k] Bhat[j][k],
+ * with Ahat = e2m1(code) * e4m3(block scale) and sA(i) = ta[0] (local_a = 0)
+ * or ta[i / 32] (local_a = 1); likewise B.  qa/sa: the row copy of A
+ * [M][K] (mx_quantize_nvfp, MX_AXIS_ROW); qb/sb: the copy of B whose stored
+ * rows are B's N columns ([N][K]: MX_AXIS_COL of a [K][N] matrix).
+ * gfx950's block-scaled matrix instruction takes power-of-two scales per
+ * 32, so the kernel dequantizes each stage exactly to f16 and multiplies
+ * on the f16 matrix cores with fp32 accumulation; alpha * sA(i) * sB(j) is
+ * one fp32 factor per output, applied once.
+ * K: a multiple of 64, at most 2^24.  M, N: any size.  qa, qb 16-byte
+ * aligned; sa, sb, ta, tb 4-byte aligned.  c: fp32 or bf16 (round to
+ * nearest even), leading dimension ldc >= N.
+ * Errors: MX_ERR_INVALID_ARG, MX_ERR_ALIGNMENT, MX_ERR_HIP.
+ */
+mx_status mx_gemm_nvfp(const uint8_t* qa, const uint8_t* sa, const float* ta, int32_t local_a,
+                       const uint8_t* qb, const uint8_t* sb, const float* tb, int32_t local_b,
+                       int64_t M, int64_t N, int64_t K, float alpha, void* c, int32_t out_dtype,
+                       int64_t ldc, void* stream);
+
 /* Static text for a status code. */
 const char* mx_status_string(mx_status status);
 

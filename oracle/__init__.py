@@ -97,6 +97,8 @@ def _load():
     L.or_nvfp_dequantize.argtypes = [_vp, _vp, _vp, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
     L.or_nvfp_gemm.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64,
                                ctypes.c_double, _vp, _vp, ctypes.c_int]
+    L.or_nvfp_gemm_entries.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _i64, _i64,
+                                       _i64, ctypes.c_double, _vp, _vp, _i64, _vp, _vp, ctypes.c_int]
     _lib = L
     return L
 
@@ -424,4 +426,20 @@ def nvfp_gemm(qa, sa, ta, local_a, qb, sb, tb, local_b, M, N, K, alpha=1.0, nthr
                               nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle: bad nvfp gemm arguments")
+    return C, bound
+
+
+def nvfp_gemm_entries(qa, sa, ta, local_a, qb, sb, tb, local_b, M, N, K, ii, jj, alpha=1.0, nthreads=None):
+    """Entries (ii, jj) of nvfp_gemm's C and bound."""
+    qa, sa, qb, sb = (np.ascontiguousarray(a, np.uint8) for a in (qa, sa, qb, sb))
+    ta, tb = np.ascontiguousarray(ta, np.float32), np.ascontiguousarray(tb, np.float32)
+    ii = np.ascontiguousarray(np.asarray(ii, np.int64))
+    jj = np.ascontiguousarray(np.asarray(jj, np.int64))
+    C = np.zeros(ii.size)
+    bound = np.zeros(ii.size)
+    rc = _load().or_nvfp_gemm_entries(_ptr(qa), _ptr(sa), _ptr(ta), int(bool(local_a)), _ptr(qb), _ptr(sb),
+                                      _ptr(tb), int(bool(local_b)), M, N, K, float(alpha), _ptr(ii), _ptr(jj),
+                                      ii.size, _ptr(C), _ptr(bound), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle: bad nvfp_gemm_entries arguments")
     return C, bound

@@ -937,24 +937,38 @@ static double nv_elem(const uint8_t* q, const uint8_t* s, int64_t K, int64_t row
     return or_decode(OR_E2M1, get_code(q, 4, K / 2, row, k)) * or_decode(OR_E4M3, s[row * (K / 16) + k / 16]);
 }
 
+/* one output entry and its bound */
+static void nvg_entry(const nvg_job* J, int64_t i, int64_t j, double* c, double* bound)
+{
+    const double sA = J->ta[J->la ? i / NV_PANEL : 0];
+    const double sB = J->tb[J->lb ? j / NV_PANEL : 0];
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < J->K; k++) {
+        const double a = nv_elem(J->qa, J->sa, J->K, i, k), b = nv_elem(J->qb, J->sb, J->K, j, k);
+        acc += a * b;
+        mag += fabs(a * b);
+    }
+    const double ap = J->alpha * sA * sB;
+    *c = ap * acc;
+    *bound = fabs(ap) * mag;
+}
+
 static void nvg_range(int64_t lo, int64_t hi, void* arg)
 {
     const nvg_job* J = (const nvg_job*)arg;
-    for (int64_t i = lo; i < hi; i++) {
-        const double sA = J->ta[J->la ? i / NV_PANEL : 0];
-        for (int64_t j = 0; j < J->N; j++) {
-            const double sB = J->tb[J->lb ? j / NV_PANEL : 0];
-            double acc = 0.0, mag = 0.0;
-            for (int64_t k = 0; k < J->K; k++) {
-                const double a = nv_elem(J->qa, J->sa, J->K, i, k), b = nv_elem(J->qb, J->sb, J->K, j, k);
-                acc += a * b;
-                mag += fabs(a * b);
-            }
-            const double ap = J->alpha * sA * sB;
-            J->C[i * J->N + j] = ap * acc;
-            J->bound[i * J->N + j] = fabs(ap) * mag;
-        }
-    }
+    for (int64_t i = lo; i < hi; i++)
+        for (int64_t j = 0; j < J->N; j++)
+            nvg_entry(J, i, j, &J->C[i * J->N + j], &J->bound[i * J->N + j]);
+}
+
+typedef struct {
+    nvg_job g; const int64_t *ii, *jj;
+} nvg_entries_job;
+
+static void nvg_entries_range(int64_t lo, int64_t hi, void* arg)
+{
+    const nvg_entries_job* E = (const nvg_entries_job*)arg;
+    for (int64_t e = lo; e < hi; e++) nvg_entry(&E->g, E->ii[e], E->jj[e], &E->g.C[e], &E->g.bound[e]);
 }
 
 /* C[i][j] = alpha * sA(i) * sB(j) * sum_k Ahat[i][k] Bhat[j][k] in double, with
@@ -967,5 +981,19 @@ int or_nvfp_gemm(const uint8_t* qa, const uint8_t* sa, const float* ta, int loca
     if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return -1;
     nvg_job J = {qa, sa, qb, sb, ta, tb, local_a, local_b, N, K, alpha, C, bound};
     parallel_for(M, nthreads, nvg_range, &J);
+    return 0;
+}
+
+/* the entries (ii[e], jj[e]) of or_nvfp_gemm's C and bound */
+int or_nvfp_gemm_entries(const uint8_t* qa, const uint8_t* sa, const float* ta, int local_a,
+                         const uint8_t* qb, const uint8_t* sb, const float* tb, int local_b,
+                         int64_t M, int64_t N, int64_t K, double alpha, const int64_t* ii, const int64_t* jj,
+                         int64_t n, double* C, double* bound, int nthreads)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0 || n < 0) return -1;
+    for (int64_t e = 0; e < n; e++)
+        if (ii[e] < 0 || ii[e] >= M || jj[e] < 0 || jj[e] >= N) return -1;
+    nvg_entries_job E = {{qa, sa, qb, sb, ta, tb, local_a, local_b, N, K, alpha, C, bound}, ii, jj};
+    parallel_for(n, nthreads, nvg_entries_range, &E);
     return 0;
 }

@@ -128,6 +128,10 @@ int or_nvfp_dequantize(const uint8_t* q, const uint8_t* s16, const float* tscale
 int or_nvfp_gemm(const uint8_t* qa, const uint8_t* sa, const float* ta, int local_a,
                  const uint8_t* qb, const uint8_t* sb, const float* tb, int local_b,
                  int64_t M, int64_t N, int64_t K, double alpha, double* C, double* bound, int nthreads);
+int or_nvfp_gemm_entries(const uint8_t* qa, const uint8_t* sa, const float* ta, int local_a,
+                         const uint8_t* qb, const uint8_t* sb, const float* tb, int local_b,
+                         int64_t M, int64_t N, int64_t K, double alpha, const int64_t* ii, const int64_t* jj,
+                         int64_t n, double* C, double* bound, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -119,3 +119,16 @@ def test_gemm_equals_float64_matmul(la, lb):
     ref = 0.5 * (sA[:, None] * sB[None, :]) * (A @ B)
     assert np.allclose(C, ref, rtol=1e-12, atol=1e-300)
     assert np.allclose(bound, 0.5 * np.abs(sA)[:, None] * np.abs(sB)[None, :] * (np.abs(A) @ np.abs(B)), rtol=1e-12)
+
+
+def test_gemm_entries_equal_full_gemm():
+    rng = np.random.default_rng(6)
+    M, N, K = 45, 37, 64
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    b = rng.standard_normal((K, N)).astype(np.float32)
+    qa, sa, ta = O.nvfp_quantize(a, O.AXIS_ROW, local=True)
+    qb, sb, tb = O.nvfp_quantize(b, O.AXIS_COL)
+    C, bound = O.nvfp_gemm(qa, sa, ta, True, qb, sb, tb, False, M, N, K, alpha=2.0)
+    ii, jj = rng.integers(0, M, 50), rng.integers(0, N, 50)
+    Ce, be = O.nvfp_gemm_entries(qa, sa, ta, True, qb, sb, tb, False, M, N, K, ii, jj, alpha=2.0)
+    assert np.array_equal(Ce, C[ii, jj]) and np.array_equal(be, bound[ii, jj])
