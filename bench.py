@@ -36,7 +36,8 @@ from fp4_quantization_block_amd import inputs as I  # noqa: E402
 from fp4_quantization_block_amd import mx  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
-MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0}   # dense scaled MFMA
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0,   # dense scaled MFMA
+                    "f16": 2500.0}                    # dense f16 MFMA (the nvfp GEMM)
 
 # HBM-side bytes per launch of the roofline kernel, from rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch) scaled by what the same
@@ -321,6 +322,47 @@ def setup_llama(args):
     return step, info
 
 
+def _setup_nvfp(local):
+    """nvfp route on the Llama-3-8B gate projection (Y = X W, X [8192][4096]
+    activations with outlier channels, W [4096][14336]): NVFP4 row copy of
+    X, column copy of W (global or CTA-local second-level scales), then the
+    GEMM that consumes them (bf16 out)."""
+    w = I.make("nvfp_llama3_8b_gate")
+    X, W = to_dev(w.tensors["X"]), to_dev(w.tensors["W"])
+    T, H = X.shape
+    F = W.shape[1]
+    qa, sa, ta = mx.mx_quantize_nvfp(X, mx.MX_AXIS_ROW, local)
+    qb, sb, tb = mx.mx_quantize_nvfp(W, mx.MX_AXIS_COL, local)
+    C = torch.empty((T, F), dtype=torch.bfloat16, device="cuda")
+
+    def step(t):
+        t.run("quant_X", lambda: mx.mx_quantize_nvfp(X, mx.MX_AXIS_ROW, local, qa, sa, ta))
+        t.run("quant_W", lambda: mx.mx_quantize_nvfp(W, mx.MX_AXIS_COL, local, qb, sb, tb))
+        t.run("gemm", lambda: mx.mx_gemm_nvfp(qa, sa, ta, local, qb, sb, tb, local, T, F, H,
+                                              out_dtype=mx.MX_OUT_BF16, c=C))
+
+    # per element 0.5 code byte and 1/16 scale byte written; the source read
+    # once per pass: two passes for the global scale (the tensor's amax must
+    # be known first), one for panel-local scales
+    passes = 1 if local else 2
+    qb_ = lambda n: passes * 2 * n + n // 2 + n // 16
+    info = dict(flops=2.0 * T * F * H, qbytes={"quant_X": qb_(T * H), "quant_W": qb_(H * F)},
+                gemm_kernel="gemm", mfma="f16", kernel_name="k_nv_gemm (f16 MFMA, exact in-loop dequantization)",
+                config={"workload": f"nvfp_{'local' if local else 'global'}_llama3_8b_gate", "M": T, "N": F,
+                        "K": H, "elem": "e2m1, e4m3 scale per 16, fp32 second-level scale "
+                        + ("per 32-row panel" if local else "per tensor"), "out": "bf16"},
+                host=w.tensors)
+    return step, info
+
+
+def setup_nvfp_global(args):
+    return _setup_nvfp(False)
+
+
+def setup_nvfp_local(args):
+    return _setup_nvfp(True)
+
+
 def setup_copy(args):
     """A plain 512 MiB device copy: the reference that scales the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) of a profiling run."""
@@ -338,7 +380,8 @@ def setup_copy(args):
 
 
 WORKLOADS = {"moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4, "llama": setup_llama,
-             "copy": setup_copy, "autoscale": setup_autoscale, "mxout": setup_mxout, "coat": setup_coat}
+             "copy": setup_copy, "autoscale": setup_autoscale, "mxout": setup_mxout, "coat": setup_coat,
+             "nvfp_global": setup_nvfp_global, "nvfp_local": setup_nvfp_local}
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -502,10 +545,11 @@ def main():
         peak = MFMA_PEAK_TFLOPS[info["mfma"]]
         roofline = {"bound": "mfma", "achieved": round(g_tf, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(g_tf / peak, 4), "traffic": measured_traffic(args.workload),
-                    "kernel": f"k_gemm_w4 ({info['mfma']} scaled MFMA)",
+                    "kernel": info.get("kernel_name", f"k_gemm_w4 ({info['mfma']} scaled MFMA)"),
                     "algorithmic": f"{info['flops']:.4g} FLOP per launch"}
         value = info["flops"] / (step_ms * 1e-3) / 1e12
-        metric = "MX GEMM TFLOP/s (% scaled-MFMA peak); mx_quantize GB/s (% HBM peak)"
+        metric = ("MX GEMM TFLOP/s (% scaled-MFMA peak); mx_quantize GB/s (% HBM peak)" if info["mfma"] != "f16"
+                  else "nvfp GEMM TFLOP/s (% f16 MFMA peak); nvfp quantize GB/s (% HBM peak)")
         unit = "TFLOP/s"
     else:
         n = names[0]
@@ -522,7 +566,8 @@ def main():
     out = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": {"fp4": "e2m1", "llama": "e4m3/e5m2"}.get(args.workload, "e4m3"),
+           "dtype": {"fp4": "e2m1", "llama": "e4m3/e5m2", "nvfp_global": "e2m1 (f16 MFMA)",
+                     "nvfp_local": "e2m1 (f16 MFMA)"}.get(args.workload, "e4m3"),
            "data": "synthetic (seeded; no weights or datasets)",
            "config": info["config"], "roofline": roofline,
            "kernels": quant, "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),

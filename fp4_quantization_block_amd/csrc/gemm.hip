@@ -307,7 +307,7 @@ void k_gemm(GArgs g)
     // lane offset, so rows past the matrix still fall outside the range.
     auto rsrc = [&](const uint8_t* base, int64_t first_row, int64_t rows, int64_t row_bytes) __attribute__((always_inline)) {
         int64_t n = (rows - first_row) * row_bytes;
-        n = n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n;
+        n = n < 0 ? 0 : n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n;
         return __builtin_amdgcn_make_buffer_rsrc((void*)(base + first_row * row_bytes), (short)0,
                                                  (int)(uint32_t)n, 0x00020000);
     };
@@ -594,20 +594,21 @@ __device__ __forceinline__ uint32_t encode_out_block(const float (&v)[32], uint3
 }
 
 // k_gemm_w4's accumulators pinned to AGPRs (see pin above)
-__device__ __forceinline__ void pin4(f16v (&acc)[4][4])
+template <int JT>
+__device__ __forceinline__ void pin4(f16v (&acc)[4][JT])
 {
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < JT; j++) asm volatile("" : "+a"(acc[i][j]));
 #endif
 }
 
-template <bool FP4>
+template <bool FP4, int JT>
 struct W4Frag {
-    typename KFrag<FP4>::V a[4], b[4];
-    uint32_t sa[4], sb[4];
+    typename KFrag<FP4>::V a[4], b[JT];
+    uint32_t sa[4], sb[JT];
 };
 
 // Non-temporal stores for k_gemm_w4's output: nothing in the kernel reads C
@@ -621,7 +622,9 @@ __device__ __forceinline__ void store_nt16(void* p, uint4 v)
     __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, (u32x4v*)p);
 }
 
-template <int FA, int FB, int OUT>
+// NB: tile columns (256, or 128 for the half tiles of a last partial round:
+// each wave then computes 128 x 64 and the B tile has 128 rows).
+template <int FA, int FB, int OUT, int NB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_w4(GArgs g)
 {
@@ -630,9 +633,13 @@ void k_gemm_w4(GArgs g)
     constexpr int EPB = FP4 ? 2 : 1;                 // elements per byte
     constexpr int KS = BKB * EPB / 64;               // MFMA k-steps per stage (2 FP8, 4 FP4)
     constexpr int SBD = KS / 2;                      // scale dwords per row per stage
-    typedef W4Frag<FP4> Frag;
+    constexpr int JT = NB / 64;                      // 32-column MFMA tiles per wave (4 or 2)
+    constexpr int RB = NB / 32;                      // 32-row load runs of the B tile (8 or 4)
+    constexpr int NM = 4 * JT;                       // MFMAs per k-step and wave
+    static_assert(NB == 256 || (NB == 128 && OUT < 2), "half tiles serve the fp32 / bf16 outputs");
+    typedef W4Frag<FP4, JT> Frag;
     __shared__ __align__(16) uint8_t lA0[TILE_BYTES], lA1[TILE_BYTES];
-    __shared__ __align__(16) uint8_t lB0[TILE_BYTES], lB1[TILE_BYTES];
+    __shared__ __align__(16) uint8_t lB0[NB * BKB], lB1[NB * BKB];
     // scale dwords of a stage, [A rows | B rows], in two planes: plane 1 holds
     // each dword shifted right by one byte, so a lane with h = 1 finds its
     // blocks at bytes 0 and 2 without a shift after the read
@@ -647,7 +654,7 @@ void k_gemm_w4(GArgs g)
 
     int tm, tn;
     tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * NB;
     const int64_t kbytes = g.K / EPB;
     const int64_t kblocks = g.K / 32;
     const int nstages = (int)(kbytes / BKB);
@@ -659,12 +666,14 @@ void k_gemm_w4(GArgs g)
     // stage's K offset rides in the unchecked scalar offset.
     auto rsrc = [&](const uint8_t* base, int64_t first_row, int64_t rows, int64_t row_bytes) __attribute__((always_inline)) {
         int64_t n = (rows - first_row) * row_bytes;
-        n = n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n;
+        n = n < 0 ? 0 : n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n;
         return __builtin_amdgcn_make_buffer_rsrc((void*)(base + first_row * row_bytes), (short)0,
                                                  (int)(uint32_t)n, 0x00020000);
     };
-    const auto ra = rsrc(g.qa, m0, g.M, kbytes), rb = rsrc(g.qb, n0, g.N, kbytes);
-    const auto rsa_ = rsrc(g.sa, m0, g.M, kblocks), rsb_ = rsrc(g.sb, n0, g.N, kblocks);
+    // B rows past the tile (a half tile's other half) also read as zero
+    const int64_t nend = min(g.N, n0 + NB);
+    const auto ra = rsrc(g.qa, m0, g.M, kbytes), rb = rsrc(g.qb, n0, nend, kbytes);
+    const auto rsa_ = rsrc(g.sa, m0, g.M, kblocks), rsb_ = rsrc(g.sb, n0, nend, kblocks);
     const int lr = tid >> 3, lc = tid & 7;
     const uint32_t voff = (uint32_t)(lr * kbytes + lc * 16);
     const uint32_t vsoff = (uint32_t)(tid * kblocks);
@@ -672,7 +681,7 @@ void k_gemm_w4(GArgs g)
     // LDS byte offset of the thread's chunk in run p: p * 32 * BKB + wofs
     const uint32_t wofs = (uint32_t)swz(lr, lc);
 
-    uint4 stA[8], stB[8];
+    uint4 stA[8], stB[RB];
     uint32_t stSA[SBD], stSB[SBD];
     // L2 warm-up: four stages ahead of its loads, each workgroup touches a
     // share of its A and B rows chosen so that the tiles sharing a panel on
@@ -684,11 +693,13 @@ void k_gemm_w4(GArgs g)
     // the fabric are what raise it.
     __shared__ __align__(16) uint8_t lPF[4 * 1024];
     const uint32_t pfa = (uint32_t)((32 * (tn & 7) + 8 * wave + (lane >> 3)) * kbytes + (lane & 7) * 16);
-    const uint32_t pfb = (uint32_t)((64 * (tm & 3) + 16 * wave + (lane >> 3)) * kbytes + (lane & 7) * 16);
+    // (half tiles: 32 B rows by tile row, one load)
+    const uint32_t pfb = (uint32_t)(((NB / 4) * (tm & 3) + (NB / 16) * wave + (lane >> 3)) * kbytes + (lane & 7) * 16);
     auto prefetch = [&](int s) __attribute__((always_inline)) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(lPF + wave * 1024), 16, pfa, s * BKB, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lPF + wave * 1024), 16, pfb, s * BKB, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lPF + wave * 1024), 16, pfb + 8 * (uint32_t)kbytes, s * BKB, 0, 0);
+        if constexpr (NB == 256)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lPF + wave * 1024), 16, pfb + 8 * (uint32_t)kbytes, s * BKB, 0, 0);
     };
     auto gl16 = [&](__amdgpu_buffer_rsrc_t r, int p, int s) __attribute__((always_inline)) {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + p * prow, s * BKB, 0));
@@ -704,16 +715,16 @@ void k_gemm_w4(GArgs g)
 #pragma unroll
         for (int p = 0; p < 8; p++) {
             stA[p] = gl16(ra, p, s);
-            stB[p] = gl16(rb, p, s);
+            if (p < RB) stB[p] = gl16(rb, p, s);
         }
         gload_scales(s);
     };
 
     // fragment reads (same lane layout and swizzle as k_gemm)
     const uint32_t oa = (uint32_t)((wm * 128 + l32) * BKB);
-    const uint32_t ob = (uint32_t)((wn * 128 + l32) * BKB);
+    const uint32_t ob = (uint32_t)((wn * (NB / 2) + l32) * BKB);
     const uint32_t hk = (uint32_t)((h ^ swz_key(l32)) << 4);
-    const int rsa = 2 * BM * SBD * h + wm * 128 + l32, rsb = 2 * BM * SBD * h + BM + wn * 128 + l32;
+    const int rsa = 2 * BM * SBD * h + wm * 128 + l32, rsb = 2 * BM * SBD * h + BM + wn * (NB / 2) + l32;
     // fragment t (0..3: A tile t, 4..7: B tile t-4) of k-step ks: FP8 holds
     // chunks 4ks + h and 4ks + 2 + h of the lane's row, FP4 chunk 2ks + h
     auto rd_frag = [&](Frag& f, const uint8_t* sA, const uint8_t* sB, int ks, int t) __attribute__((always_inline)) {
@@ -749,16 +760,16 @@ void k_gemm_w4(GArgs g)
     auto swrite_a = [&](uint8_t* sA, int p) __attribute__((always_inline)) { *(uint4*)(sA + p * 32 * BKB + wofs) = stA[p]; };
     auto swrite_b = [&](uint8_t* sB, int p) __attribute__((always_inline)) { *(uint4*)(sB + p * 32 * BKB + wofs) = stB[p]; };
 
-    f16v acc[4][4];
+    f16v acc[4][JT];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < JT; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
     auto mma = [&](const Frag& f, int ks, int m) __attribute__((always_inline)) {
-        const int i = m >> 2, j = m & 3;
+        const int i = m / JT, j = m % JT;
         if ((ks & 1) == 0)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mfma_src<FP4>(f.a[i]), mfma_src<FP4>(f.b[j]), acc[i][j],
                                                                         MfmaFmt<FA>::code, MfmaFmt<FB>::code, 0, (int)f.sa[i], 0, (int)f.sb[j]);
@@ -776,11 +787,11 @@ void k_gemm_w4(GArgs g)
     {
         const int s1 = min(1, nstages - 1);
         gload(0);
-        uint4 uA[8], uB[8];
+        uint4 uA[8], uB[RB];
 #pragma unroll
         for (int p = 0; p < 8; p++) {
             uA[p] = gl16(ra, p, s1);
-            uB[p] = gl16(rb, p, s1);
+            if (p < RB) uB[p] = gl16(rb, p, s1);
         }
         uint32_t uSA[SBD], uSB[SBD];
 #pragma unroll
@@ -791,14 +802,14 @@ void k_gemm_w4(GArgs g)
 #pragma unroll
         for (int p = 0; p < 8; p++) {
             swrite_a(lA0, p);
-            swrite_b(lB0, p);
+            if (p < RB) swrite_b(lB0, p);
         }
         wr_scales(lS0);
 #pragma unroll
         for (int p = 0; p < 8; p++) {
             stA[p] = gl16(ra, p, min(2, nstages - 1));
             *(uint4*)(lA1 + p * 32 * BKB + wofs) = uA[p];
-            stB[p] = uB[p];
+            if (p < RB) stB[p] = uB[p];
         }
 #pragma unroll
         for (int d = 0; d < SBD; d++) {
@@ -811,9 +822,9 @@ void k_gemm_w4(GArgs g)
     prefetch(min(3, nstages - 1));
     half_barrier();
 #pragma unroll
-    for (int q = 0; q < 8; q++) rd_frag(F0, lA0, lB0, 0, q);
+    for (int q = 0; q < 4 + JT; q++) rd_frag(F0, lA0, lB0, 0, q);
 #pragma unroll
-    for (int t = 0; t < 8; t++) rd_scale(F0, lS0, t, 0);
+    for (int t = 0; t < 4 + JT; t++) rd_scale(F0, lS0, t, 0);
 
     // Stage s computes from buffer X and fills buffer Y with stage s+1 and
     // X with stage s+2.  Each k-step is a phase of 16 MFMAs from one
@@ -826,39 +837,46 @@ void k_gemm_w4(GArgs g)
     // second writes the scales; the last phase, after the barrier that
     // ends every read of X, writes stage s+2's A tile to X and reloads it
     // with stage s+3.  Each register-held tile has a whole stage to arrive.
+    // (Half tiles: 8 MFMAs per phase; each slot reads one fragment and its
+    // scale, and the last phase writes an A run after every MFMA.)
     auto phase = [&](auto KSC, int s, Frag& cur, Frag& nxt, uint8_t* xA, const uint8_t* xB, const uint32_t* xS,
                      uint8_t* yA, uint8_t* yB, uint32_t* yS) __attribute__((always_inline)) {
         constexpr int ks = decltype(KSC)::value;
         constexpr bool last = ks == KS - 1;
         const int s2 = min(s + 2, nstages - 1), s3 = min(s + 3, nstages - 1);
 #pragma unroll
-        for (int m = 0; m < 16; m++) {
+        for (int m = 0; m < NM; m++) {
             mma(cur, ks, m);
             __builtin_amdgcn_sched_barrier(0);
-            if (m < 8) {
-                if constexpr (last) rd_frag(nxt, yA, yB, 0, m);
-                else rd_frag(nxt, xA, xB, ks + 1, m);
-            } else {
-                if constexpr (last) rd_scale(nxt, yS, m - 8, 0);
-                else rd_scale(nxt, xS, m - 8, ks + 1);
+            const bool rf = NB == 256 ? m < 8 : m < 4 + JT;          // fragment read in this slot
+            const bool rs = NB == 256 ? m >= 8 : m < 4 + JT;         // scale read in this slot
+            const int qf = m, qs = NB == 256 ? m - 8 : m;
+            if (rf) {
+                if constexpr (last) rd_frag(nxt, yA, yB, 0, qf);
+                else rd_frag(nxt, xA, xB, ks + 1, qf);
+            }
+            if (rs) {
+                if constexpr (last) rd_scale(nxt, yS, qs, 0);
+                else rd_scale(nxt, xS, qs, ks + 1);
             }
             if constexpr (ks == 0) {
-                if (m < 8) {
+                if (m < RB) {
                     swrite_b(yB, m);
                     stB[m] = gl16(rb, m, s2);
                 }
-                if (m == 9) prefetch(min(s + 4, nstages - 1));
+                if (m == (NB == 256 ? 9 : 5)) prefetch(min(s + 4, nstages - 1));
             }
             if constexpr (ks == (KS == 2 ? 0 : 1)) {
-                if (m == 8) {
+                if (m == (NB == 256 ? 8 : 6)) {
                     wr_scales(yS);
                     gload_scales(s2);
                 }
             }
             if constexpr (last) {
-                if (m >= 8) {
-                    swrite_a(xA, m - 8);
-                    stA[m - 8] = gl16(ra, m - 8, s3);
+                const int p = NB == 256 ? m - 8 : m;
+                if (p >= 0) {
+                    swrite_a(xA, p);
+                    stA[p] = gl16(ra, p, s3);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -888,32 +906,35 @@ void k_gemm_w4(GArgs g)
     half_barrier();                                  // every wave done with the stage buffers
 
     if constexpr (OUT == 1) {
-        // each wave stages its 128x128 quarter (256-byte rows) in 32 KiB of LDS
+        // each wave stages its 128 x NB/2 part (NB-byte rows) in LDS: 32 KiB
+        // (half tiles 16 KiB, the size of a B stage buffer)
+        constexpr int WC = NB / 2;                   // columns per wave
         uint8_t* buf = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
         uint16_t* ct = (uint16_t*)buf;
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < JT; j++)
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {     // rows r and r + 1 of the accumulator
                     const int row = i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                     const int col = j * 32 + l32;
                     const uint32_t u = f32x2_to_bf16x2_rne(acc[i][j][r] * ap, acc[i][j][r + 1] * ap);
-                    ct[row * 128 + col] = (uint16_t)u;
-                    ct[(row + 1) * 128 + col] = (uint16_t)(u >> 16);
+                    ct[row * WC + col] = (uint16_t)u;
+                    ct[(row + 1) * WC + col] = (uint16_t)(u >> 16);
                 }
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
         const bool vec = (g.ldc % 8) == 0 && (((uintptr_t)g.c) & 15u) == 0;
-        const int64_t rbase = m0 + wm * 128, cbase = n0 + wn * 128;
+        const int64_t rbase = m0 + wm * 128, cbase = n0 + wn * WC;
+        constexpr int CPR = WC / 8;                  // 16-byte chunks per row
 #pragma unroll 4
-        for (int p = 0; p < 32; p++) {
+        for (int p = 0; p < 128 * CPR / 64; p++) {
             const int id = p * 64 + lane;
-            const int row = id >> 4, c8 = (id & 15) * 8;
+            const int row = id / CPR, c8 = (id % CPR) * 8;
             const int64_t grow = rbase + row, gcol = cbase + c8;
             if (grow >= g.M) continue;
-            const uint4 v = *(const uint4*)(ct + row * 128 + c8);
+            const uint4 v = *(const uint4*)(ct + row * WC + c8);
             uint16_t* dst = (uint16_t*)g.c + grow * g.ldc + gcol;
             if (vec && gcol + 8 <= g.N) {
                 store_nt16(dst, v);
@@ -969,8 +990,8 @@ void k_gemm_w4(GArgs g)
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int64_t col = n0 + wn * 128 + j * 32 + l32;
+            for (int j = 0; j < JT; j++) {
+                const int64_t col = n0 + wn * (NB / 2) + j * 32 + l32;
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
@@ -981,13 +1002,46 @@ void k_gemm_w4(GArgs g)
 #endif
 }
 
+int cu_count()
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return cus;
+}
+
 template <int FA, int FB, int OUT>
 hipError_t launch3(const GArgs& a, hipStream_t s)
 {
     const unsigned nwg = (unsigned)(a.tiles_m * a.tiles_n);
     constexpr int EPB = FA == E2M1 ? 2 : 1;
     if (!a.reg_path && (a.K / EPB) % BKB == 0) {
-        k_gemm_w4<FA, FB, OUT><<<dim3(nwg), dim3(256), 0, s>>>(a);
+        if constexpr (OUT < 2) {
+            // Last partial round: with one 256x256 tile per CU at a time, a
+            // grid of R full rounds plus r < CUs/2 tiles takes R + 1 rounds
+            // of time.  When the r tiles are whole tile rows, they run as a
+            // second launch of 2r half tiles (256 x 128), which takes half
+            // a round.  (E.g. 6144 x 4096: 384 tiles on 256 CUs.)
+            const int cus = cu_count();
+            const int total = (int)nwg, r = total % cus;
+            if (total > cus && r != 0 && r % a.tiles_n == 0 && 2 * r <= cus) {
+                const int tr = r / a.tiles_n;
+                GArgs head = a, tail = a;
+                head.tiles_m = a.tiles_m - tr;
+                head.M = (int64_t)head.tiles_m * BM;
+                const int64_t kbytes = a.K / EPB, kblocks = a.K / 32;
+                const size_t es = OUT == 1 ? 2 : 4;
+                tail.qa = a.qa + head.M * kbytes;
+                tail.sa = a.sa + head.M * kblocks;
+                tail.c = (uint8_t*)a.c + (size_t)(head.M * a.ldc) * es;
+                tail.M = a.M - head.M;
+                tail.tiles_m = tr;
+                tail.tiles_n = (int)((a.N + 127) / 128);
+                k_gemm_w4<FA, FB, OUT, 256><<<dim3(head.tiles_m * head.tiles_n), dim3(256), 0, s>>>(head);
+                k_gemm_w4<FA, FB, OUT, 128><<<dim3(tail.tiles_m * tail.tiles_n), dim3(256), 0, s>>>(tail);
+                return hipGetLastError();
+            }
+        }
+        k_gemm_w4<FA, FB, OUT, 256><<<dim3(nwg), dim3(256), 0, s>>>(a);
         return hipGetLastError();
     }
     if constexpr (OUT >= 2) {

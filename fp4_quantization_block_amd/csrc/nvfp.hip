@@ -273,7 +273,7 @@ void k_nv_gemm(NvGemmJob g, int tiles_m, int tiles_n)
 
     auto rsrc = [&](const uint8_t* base, int64_t first_row, int64_t rows, int64_t row_bytes) __attribute__((always_inline)) {
         int64_t n = (rows - first_row) * row_bytes;
-        n = n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n;
+        n = n < 0 ? 0 : n > 0xFFFFFFFFll ? 0xFFFFFFFFll : n;
         return __builtin_amdgcn_make_buffer_rsrc((void*)(base + first_row * row_bytes), (short)0, (int)(uint32_t)n,
                                                  0x00020000);
     };
@@ -365,7 +365,7 @@ unsigned nv_grid(int64_t items)
 {
     int64_t wg = (items + 255) / 256;
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t cap = (int64_t)cus * 16;
     return (unsigned)(wg < 1 ? 1 : (wg < cap ? wg : cap));
 }

@@ -199,7 +199,7 @@ unsigned grid_for(int64_t nthreads)
 {
     int64_t wg = (nthreads + 255) / 256;
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t cap = (int64_t)cus * 16;
     return (unsigned)(wg < cap ? (wg < 1 ? 1 : wg) : cap);
 }

@@ -251,3 +251,42 @@ def test_full_llama3_8b_mlp():
         C, bound = O.gemm_entries(qao, sao, None, fa, qbo, sbo, None, fb, M, N, K, ii, jj)
         _report("llama3_8b_mlp", gname, (M, N, K), fa, fb, got, C, bound, K, 1.0, qao, sao, qbo, sbo, ii, jj,
                 sampled="16 per 128x128 tile incl. corners")
+
+
+@pytest.mark.parametrize("fmt,K,out", [("e4m3", 256, "f32"), ("e4m3", 384, "bf16"), ("e2m1", 512, "f32"),
+                                       ("e2m1", 768, "bf16")])
+def test_last_round_half_tiles(fmt, K, out):
+    """A grid of one full round of 256 x 256 tiles plus one tile row: the
+    last tile row runs as a second launch of 256 x 128 half tiles.  Ragged M
+    (the tail row holds 100 rows) and N (300: the third half tile holds 44
+    columns).  Every output of the tail rows, the rows next to the seam and
+    a sample of the rest are checked."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles_m = cus // 2 + 1                                  # x 2 tile columns = cus + 2 tiles
+    M, N = (tiles_m - 1) * 256 + 100, 300
+    rng = np.random.default_rng(K + len(fmt))
+    a = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-3, 4, (M, 1)))).astype(np.float32)
+    b = (rng.standard_normal((K, N)) * 0.05).astype(np.float32)
+    log(f"half-tile tail {fmt} {M}x{N}x{K} out={out} ({cus} CUs)")
+    (qa, sa, _), (qao, sao, _) = quant_both(a, O.AXIS_ROW, fmt)
+    (qb, sb, _), (qbo, sbo, _) = quant_both(b, O.AXIS_COL, fmt)
+    od = mx.MX_OUT_F32 if out == "f32" else mx.MX_OUT_BF16
+    c = mx.mx_gemm(qa, sa, None, fmt, qb, sb, None, fmt, M, N, K, alpha=0.5, out_dtype=od)
+    torch.cuda.synchronize()
+    seam = (tiles_m - 1) * 256
+    rows = np.concatenate([np.arange(seam - 8, M), rng.integers(0, seam - 8, 64)])
+    ii = np.repeat(rows, N).astype(np.int64)
+    jj = np.tile(np.arange(N), rows.size).astype(np.int64)
+    C, bound = O.gemm_entries(qao, sao, None, fmt, qbo, sbo, None, fmt, M, N, K, ii, jj, alpha=0.5)
+    got = _pick(c, ii, jj)
+    if out == "f32":
+        _report("half_tile_tail", fmt, (M, N, K), fmt, fmt, got, C, bound, K, 0.5,
+                O.unpack_codes(qao, fmt) if O.elem_bits(fmt) == 8 else None, sao,
+                O.unpack_codes(qbo, fmt) if O.elem_bits(fmt) == 8 else None, sbo, ii, jj,
+                sampled="tail rows, seam rows, 64 random rows")
+    else:
+        allow = None
+        if O.elem_bits(fmt) == 8:
+            allow = mfma_rule(O.unpack_codes(qao, fmt), sao, fmt, O.unpack_codes(qbo, fmt), sbo, fmt, 0.5,
+                              ii, jj)[1]
+        gemm_check(got, C, bound, True, f"half-tile tail {fmt} bf16", allow)
