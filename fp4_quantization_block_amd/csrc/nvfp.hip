@@ -34,6 +34,8 @@
 // the main-loop dequantization that [MOSS, "GEMM Kernel 优化"] shows eating
 // the gain -- the price of this scale domain on this hardware: the f16
 // matrix peak is a quarter of the FP4 one.
+#include <algorithm>
+
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -68,108 +70,233 @@ __device__ __forceinline__ float e4m3_value(uint32_t c)
     return (c & 0x80u) ? -v : v;
 }
 
-// ---------------------------------------------------------------------------
-// second-level scales
-// ---------------------------------------------------------------------------
-// amax key (|x| bits; NaN above Inf above finite) of stored rows
-// [32 p, 32 p + 32) of the copy, one workgroup per panel p
-template <int SRC, bool ROW>
-__global__ __launch_bounds__(256) void k_nv_panel_amax(const void* x, int64_t rows, int64_t cols, int64_t ld,
-                                                       int64_t npanels, int local, float* ts, uint32_t* keys)
+// 8 consecutive source elements from x[i] (16-byte aligned) as floats
+template <int SRC> __device__ __forceinline__ void load8(const void* x, int64_t i, float* v)
 {
-    const int64_t SR = ROW ? rows : cols, L = ROW ? cols : rows;
-    for (int64_t p = blockIdx.x; p < npanels; p += gridDim.x) {
-        const int64_t r0 = p * NV_PANEL, r1 = min(r0 + NV_PANEL, SR);
+    if constexpr (SRC == SRC_BF16) {
+        const uint4 u = *(const uint4*)((const uint16_t*)x + i);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 a = *(const float4*)((const float*)x + i), b = *(const float4*)((const float*)x + i + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+// x[r][c0 .. c0+7] (zero past `cols`), vectorized when `vec` (16-byte
+// aligned rows, cols % 8 == 0)
+template <int SRC>
+__device__ __forceinline__ void row8(const void* x, int64_t ld, int64_t cols, bool vec, int64_t r, int64_t c0, float* v)
+{
+    if (vec && c0 + 8 <= cols) {
+        load8<SRC>(x, r * ld + c0, v);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = c0 + k < cols ? src_at<SRC>(x, r * ld + c0 + k) : 0.0f;
+    }
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
+
+// second-level scale of a domain from its amax key: NaN for a NaN or Inf, 1
+// for an all-zero domain, else amax / (6 * 448)
+__device__ __forceinline__ float domain_scale(uint32_t key)
+{
+    return key >= 0x7F800000u ? __builtin_nanf("") : key == 0 ? 1.0f : __uint_as_float(key) / 2688.0f;
+}
+
+// ---------------------------------------------------------------------------
+// second-level scales: per-panel amax partials, then the scales
+// ---------------------------------------------------------------------------
+// Element tiles are 32 source rows x 256 source columns.  A panel (32
+// stored rows) is a tile row of the source for the row copy and eight
+// consecutive 32-column strips for the column copy.  Workgroup (a, g) takes
+// tile a across the panels and S consecutive tiles along them (tiles
+// g*S ..), reducing to one amax key per panel it touches:
+//   row copy:    partial[a * G + g]             (panel a)
+//   column copy: partial[(8 a + k) * G + g]     (panels 8a + k, k < 8)
+// Thread t reads 8 columns (chunk t % 32) of rows t / 32 + 8 i, i < 4, of a
+// tile: 16- or 32-byte loads, 128 contiguous bytes per wave row.
+template <int SRC, bool ROW>
+__global__ __launch_bounds__(256) void k_nv_amax(const void* x, int64_t rows, int64_t cols, int64_t ld, bool vec,
+                                                 int tiles_across, int tiles_along, int S, int G, int64_t npanels,
+                                                 uint32_t* partial)
+{
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, cc = t & 31;
+    __shared__ uint32_t red[4][8];
+    for (int64_t w = blockIdx.x; w < (int64_t)tiles_across * G; w += gridDim.x) {
+        const int a = (int)(w / G), g = (int)(w % G);
         uint32_t key = 0;
-        if (ROW) {                                   // panel rows are source rows: walk each along its length
-            for (int64_t r = r0; r < r1; r++)
-                for (int64_t c = threadIdx.x; c < L; c += 256)
-                    key = max(key, __float_as_uint(src_at<SRC>(x, r * ld + c)) & 0x7FFFFFFFu);
-        } else {                                     // panel rows are source columns: 32 per source row
-            for (int64_t i = threadIdx.x; i < (r1 - r0) * L; i += 256) {
-                const int64_t r = i / (r1 - r0), c = r0 + i % (r1 - r0);
-                key = max(key, __float_as_uint(src_at<SRC>(x, r * ld + c)) & 0x7FFFFFFFu);
+        for (int e = g * S; e < min(g * S + S, tiles_along); e++) {
+            const int tr = ROW ? a : e, tc = ROW ? e : a;
+            const int64_t c0 = (int64_t)tc * 256 + 8 * cc;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int64_t r = (int64_t)tr * 32 + (t >> 5) + 8 * i;
+                if (r < rows && c0 < cols) {
+                    float v[8];
+                    row8<SRC>(x, ld, cols, vec, r, c0, v);
+#pragma unroll
+                    for (int k = 0; k < 8; k++) key = max(key, abs_bits(v[k]));
+                }
             }
         }
+        if (ROW) {                                   // one panel: the whole workgroup
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
-        __shared__ uint32_t red[4];
-        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = key;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            key = max(max(red[0], red[1]), max(red[2], red[3]));
-            if (local) {
-                ts[p] = key >= 0x7F800000u ? __builtin_nanf("") : key == 0 ? 1.0f : __uint_as_float(key) / 2688.0f;
-            } else {
-                keys[p] = key;
+            for (int m = 1; m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
+            if (lane == 0) red[wave][0] = key;
+            __syncthreads();
+            if (t == 0) partial[(int64_t)a * G + g] = max(max(red[0][0], red[1][0]), max(red[2][0], red[3][0]));
+        } else {                                     // panel of chunk cc: 8 a + cc / 4
+            key = max(key, (uint32_t)__shfl_xor((int)key, 1));
+            key = max(key, (uint32_t)__shfl_xor((int)key, 2));
+            key = max(key, (uint32_t)__shfl_xor((int)key, 32));
+            if (lane < 32 && (lane & 3) == 0) red[wave][lane >> 2] = key;
+            __syncthreads();
+            if (t < 8) {
+                const int64_t p = 8 * (int64_t)a + t;
+                if (p < npanels) partial[p * G + g] = max(max(red[0][t], red[1][t]), max(red[2][t], red[3][t]));
             }
         }
         __syncthreads();
     }
 }
 
-// global: one workgroup reduces the panel keys into the tensor's scale
-__global__ __launch_bounds__(256) void k_nv_global_scale(const uint32_t* keys, int64_t n, float* ts)
+// CTA-local: ts[p] from the G partials of panel p
+__global__ __launch_bounds__(256) void k_nv_scales_local(const uint32_t* partial, int64_t npanels, int G, float* ts)
+{
+    for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < npanels; p += (int64_t)gridDim.x * 256) {
+        uint32_t key = 0;
+        for (int g = 0; g < G; g++) key = max(key, partial[p * G + g]);
+        ts[p] = domain_scale(key);
+    }
+}
+
+// global: ts[0] from all n partials, one workgroup
+__global__ __launch_bounds__(1024) void k_nv_scale_global(const uint32_t* partial, int64_t n, float* ts)
 {
     uint32_t key = 0;
-    for (int64_t i = threadIdx.x; i < n; i += 256) key = max(key, keys[i]);
+    for (int64_t i = threadIdx.x; i < n; i += 1024) key = max(key, partial[i]);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
-    __shared__ uint32_t red[4];
+    __shared__ uint32_t red[16];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = key;
     __syncthreads();
     if (threadIdx.x == 0) {
-        key = max(max(red[0], red[1]), max(red[2], red[3]));
-        ts[0] = key >= 0x7F800000u ? __builtin_nanf("") : key == 0 ? 1.0f : __uint_as_float(key) / 2688.0f;
+        for (int i = 1; i < 16; i++) key = max(key, red[i]);
+        ts[0] = domain_scale(key);
     }
 }
 
 // ---------------------------------------------------------------------------
-// quantize: one thread per block of 16 along the stored row
+// quantize
 // ---------------------------------------------------------------------------
-template <int SRC, bool ROW>
-__global__ __launch_bounds__(256) void k_nv_quant(const void* x, int64_t rows, int64_t cols, int64_t ld, int local,
-                                                  const float* ts, uint8_t* q, uint8_t* s16)
+// one block of 16 values under second-level scale s: returns the E4M3
+// scale byte, writes the 16 E2M1 codes (element 2j in the low nibble of
+// byte j) to w[0..1]
+__device__ __forceinline__ uint32_t nv_block(const float* v, float s, uint32_t* w)
 {
-    const int64_t SR = ROW ? rows : cols, L = ROW ? cols : rows, nb = L / 16, total = SR * nb;
+    uint32_t key = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) key = max(key, abs_bits(v[i]));
+    w[0] = w[1] = 0;
+    if (key >= 0x7F800000u || s != s) return 0x7Fu;
+    const float den = 6.0f * s;
+    const float bv = __uint_as_float(key) / den;
+    const uint32_t sb = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fmax<E4M3>(bv), 0.0f, 0, false) & 0x7Fu;
+    const float ds = e4m3_value(sb);
+    if (ds == 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) w[0] |= (__float_as_uint(v[i]) >> 31) << (4 * i + 3);
+#pragma unroll
+        for (int i = 0; i < 8; i++) w[1] |= (__float_as_uint(v[8 + i]) >> 31) << (4 * i + 3);
+    } else {
+        const float d = ds * s;
+        const float r = 1.0f / d;
+        float y[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) y[i] = clamp_fmax<E2M1>(v[i] * r);
+        w[0] = cvt8_fp4(y);
+        w[1] = cvt8_fp4(y + 8);
+    }
+    return sb;
+}
+
+// row copy: one thread per block of 16 along the source row; consecutive
+// threads take consecutive blocks (32- or 64-byte loads)
+template <int SRC>
+__global__ __launch_bounds__(256) void k_nv_quant_row(const void* x, int64_t rows, int64_t cols, int64_t ld, bool vec,
+                                                      int local, const float* ts, uint8_t* q, uint8_t* s16)
+{
+    const int64_t nb = cols / 16, total = rows * nb;
     for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
-        // row copy: consecutive threads walk a stored row's blocks; column copy:
-        // consecutive threads take neighbouring source columns (coalesced reads)
-        const int64_t sr = ROW ? t / nb : t % SR, b = ROW ? t % nb : t / SR;
-        const float s = ts[local ? sr / NV_PANEL : 0];
+        const int64_t r = t / nb, b = t % nb;
         float v[16];
+        row8<SRC>(x, ld, cols, vec, r, b * 16, v);
+        row8<SRC>(x, ld, cols, vec, r, b * 16 + 8, v + 8);
+        uint32_t w[2];
+        const uint32_t sb = nv_block(v, ts[local ? r / NV_PANEL : 0], w);
+        s16[t] = (uint8_t)sb;
+        *(uint2*)(q + r * (cols / 2) + b * 8) = make_uint2(w[0], w[1]);
+    }
+}
+
+// column copy: tiles of 128 source rows x 64 source columns staged through
+// LDS (fp32, rows padded to 65).  Loads: 8 columns of a row per thread per
+// step, rows of 128 contiguous bytes (bf16).  Quantization: thread t takes
+// column t / 4 and its blocks 2 (t % 4) and 2 (t % 4) + 1, so four
+// consecutive lanes write one stored row's 64 contiguous code bytes.
+template <int SRC>
+__global__ __launch_bounds__(256) void k_nv_quant_col(const void* x, int64_t rows, int64_t cols, int64_t ld, bool vec,
+                                                      int local, const float* ts, uint8_t* q, uint8_t* s16)
+{
+    constexpr int TR = 128, TC = 64, PAD = TC + 1;
+    __shared__ float tile[TR * PAD];
+    const int t = threadIdx.x;
+    const int64_t tiles_r = (rows + TR - 1) / TR, tiles_c = (cols + TC - 1) / TC;
+    const int64_t nb = rows / 16;                    // blocks per stored row
+    for (int64_t w = blockIdx.x; w < tiles_r * tiles_c; w += gridDim.x) {
+        const int64_t r0 = (w / tiles_c) * TR, c0 = (w % tiles_c) * TC;
+        // 128 rows x 8 chunks of 8 columns: 4 per thread
 #pragma unroll
-        for (int i = 0; i < 16; i++)
-            v[i] = ROW ? src_at<SRC>(x, sr * ld + b * 16 + i) : src_at<SRC>(x, (b * 16 + i) * ld + sr);
-        uint32_t key = 0;
+        for (int i = 0; i < 4; i++) {
+            const int id = t + 256 * i, rr = id >> 3, ch = id & 7;
+            const int64_t r = r0 + rr, c = c0 + 8 * ch;
+            float v[8];
+            if (r < rows && c < cols) row8<SRC>(x, ld, cols, vec, r, c, v);
+            else {
 #pragma unroll
-        for (int i = 0; i < 16; i++) key = max(key, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-        uint32_t sb;
-        uint32_t w0 = 0, w1 = 0;                     // 16 codes
-        if (key >= 0x7F800000u || s != s) {
-            sb = 0x7Fu;
-        } else {
-            const float den = 6.0f * s;
-            const float bv = __uint_as_float(key) / den;
-            sb = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fmax<E4M3>(bv), 0.0f, 0, false) & 0x7Fu;
-            const float ds = e4m3_value(sb);
-            if (ds == 0.0f) {
+                for (int k = 0; k < 8; k++) v[k] = 0.0f;
+            }
 #pragma unroll
-                for (int i = 0; i < 8; i++) w0 |= (__float_as_uint(v[i]) >> 31) << (4 * i + 3);
+            for (int k = 0; k < 8; k++) tile[rr * PAD + 8 * ch + k] = v[k];
+        }
+        __syncthreads();
+        const int cl = t >> 2, bp = t & 3;
+        const int64_t sr = c0 + cl;                  // stored row = source column
+        if (sr < cols) {
+            const float s = ts[local ? sr / NV_PANEL : 0];
 #pragma unroll
-                for (int i = 0; i < 8; i++) w1 |= (__float_as_uint(v[8 + i]) >> 31) << (4 * i + 3);
-            } else {
-                const float d = ds * s;
-                const float r = 1.0f / d;
-                float y[16];
+            for (int h = 0; h < 2; h++) {
+                const int blk = 2 * bp + h;          // block within the tile (rows 16 blk ..)
+                const int64_t bi = r0 / 16 + blk;    // block within the stored row
+                if (bi < nb) {
+                    float v[16];
 #pragma unroll
-                for (int i = 0; i < 16; i++) y[i] = clamp_fmax<E2M1>(v[i] * r);
-                w0 = cvt8_fp4(y);
-                w1 = cvt8_fp4(y + 8);
+                    for (int i = 0; i < 16; i++) v[i] = tile[(16 * blk + i) * PAD + cl];
+                    uint32_t wq[2];
+                    const uint32_t sb = nv_block(v, s, wq);
+                    s16[sr * nb + bi] = (uint8_t)sb;
+                    *(uint2*)(q + sr * (rows / 2) + bi * 8) = make_uint2(wq[0], wq[1]);
+                }
             }
         }
-        s16[sr * nb + b] = (uint8_t)sb;
-        *(uint2*)(q + sr * (L / 2) + b * 8) = make_uint2(w0, w1);
+        __syncthreads();
     }
 }
 
@@ -373,15 +500,34 @@ unsigned nv_grid(int64_t items)
 template <int SRC, bool ROW>
 hipError_t launch_nv_quant(const NvQuantJob& j, hipStream_t st)
 {
-    const int64_t SR = ROW ? j.rows : j.cols, L = ROW ? j.cols : j.rows;
+    const int64_t SR = ROW ? j.rows : j.cols;
     const int64_t npanels = (SR + NV_PANEL - 1) / NV_PANEL;
-    const unsigned pg = (unsigned)(npanels < 4096 ? npanels : 4096);
-    // global: per-panel keys parked in the code array, which the quantize
-    // kernel overwrites afterwards (SR * L / 2 >= 8 * SR >= 4 * npanels bytes)
-    k_nv_panel_amax<SRC, ROW><<<pg, 256, 0, st>>>(j.x, j.rows, j.cols, j.ld, npanels, j.local, j.ts,
-                                                   (uint32_t*)j.q);
-    if (!j.local) k_nv_global_scale<<<1, 256, 0, st>>>((const uint32_t*)j.q, npanels, j.ts);
-    k_nv_quant<SRC, ROW><<<nv_grid(SR * (L / 16)), 256, 0, st>>>(j.x, j.rows, j.cols, j.ld, j.local, j.ts, j.q, j.s16);
+    const int64_t es = SRC == SRC_BF16 ? 2 : 4;
+    const bool vec = ((uintptr_t)j.x % 16) == 0 && (j.ld * es) % 16 == 0 && j.cols % 8 == 0;
+    // amax partials: about 2048 workgroups; parked in the code array, which
+    // the quantize kernel overwrites afterwards (npanels * G * 4 bytes is at
+    // most rows * cols / 4, the array holds rows * cols / 2)
+    const int tiles_r = (int)((j.rows + 31) / 32), tiles_c = (int)((j.cols + 255) / 256);
+    const int across = ROW ? tiles_r : tiles_c, along = ROW ? tiles_c : tiles_r;
+    int G = (int)std::max<int64_t>(1, std::min<int64_t>(along, 2048 / std::max(1, across)));
+    const int S = (along + G - 1) / G;
+    G = (along + S - 1) / S;
+    uint32_t* partial = (uint32_t*)j.q;
+    const int64_t nwg = (int64_t)across * G;
+    k_nv_amax<SRC, ROW><<<(unsigned)std::min<int64_t>(nwg, 65535), 256, 0, st>>>(j.x, j.rows, j.cols, j.ld, vec, across,
+                                                                                  along, S, G, npanels, partial);
+    if (j.local)
+        k_nv_scales_local<<<(unsigned)((npanels + 255) / 256), 256, 0, st>>>(partial, npanels, G, j.ts);
+    else
+        k_nv_scale_global<<<1, 1024, 0, st>>>(partial, npanels * G, j.ts);
+    if (ROW) {
+        k_nv_quant_row<SRC><<<nv_grid(j.rows * (j.cols / 16)), 256, 0, st>>>(j.x, j.rows, j.cols, j.ld, vec, j.local,
+                                                                            j.ts, j.q, j.s16);
+    } else {
+        const int64_t tiles = ((j.rows + 127) / 128) * ((j.cols + 63) / 64);
+        k_nv_quant_col<SRC><<<(unsigned)std::min<int64_t>(tiles, 65535), 256, 0, st>>>(j.x, j.rows, j.cols, j.ld, vec,
+                                                                                      j.local, j.ts, j.q, j.s16);
+    }
     return hipGetLastError();
 }
 

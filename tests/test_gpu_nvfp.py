@@ -81,6 +81,17 @@ def test_quantize_and_dequantize_match_oracle(axis, local, src):
 
 
 @pytest.mark.parametrize("local", [False, True])
+@pytest.mark.parametrize("axis", [mx.MX_AXIS_ROW, mx.MX_AXIS_COL])
+def test_unaligned_rows(axis, local):
+    """Row starts off 16-byte alignment (ld = cols + 3): the element-wise
+    load path, bit-exact as the vector one."""
+    rng = np.random.default_rng(50 + 2 * axis + local)
+    rows, cols = (96, 208) if axis == mx.MX_AXIS_ROW else (208, 100)
+    x = _source(rng, rows, cols, "bf16")
+    _compare_copy(x, axis, local, f"unaligned axis={axis} local={local}", ld_pad=3)
+
+
+@pytest.mark.parametrize("local", [False, True])
 def test_special_values(local):
     """A NaN poisons its domain: the whole tensor (global) or its panel
     (local); Inf likewise; an all-zero domain gets scale 1."""
