@@ -341,6 +341,10 @@ __global__ __launch_bounds__(256) void k_nv_dequant(const uint8_t* q, const uint
 // XOR-swizzled by (row >> 1) & 7, conflict-free for the fragment reads).
 // The second-level scales are applied once per output in the epilogue.
 // ---------------------------------------------------------------------------
+// workgroup barrier that waits for this wave's LDS traffic only (not for
+// its global loads, which a fence-carrying __syncthreads would drain)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f16acc __attribute__((ext_vector_type(16)));
@@ -350,30 +354,24 @@ constexpr int NBM = 256, NBK = 64, NROWB = NBK * 2;   // tile rows, K per stage,
 __device__ __forceinline__ int nv_swz(int row, int chunk) { return row * NROWB + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // one 16-byte chunk of codes (32 elements, two blocks) and its two block
-// scales -> 32 exact f16 values into LDS row `row`, chunks 4*half .. 4*half+3
+// scales -> 32 exact f16 values into LDS row `row`, chunks 4*half .. 4*half+3.
+// Both converters are exact here: the FP4 one (scale 1) gives the E2M1
+// values, the FP8 one gives the two E4M3 block scales (every E4M3 value,
+// subnormals and NaN included, is an f16), and their product has at most
+// 6 significant bits and lies in [2^-10, 2688] -- an f16, so the packed
+// multiply does not round.
 __device__ __forceinline__ void nv_dequant_chunk(uint8_t* tile, int row, int half, uint4 codes, uint32_t sc2)
 {
-    float p2[2];
-    _Float16 fct[2];
-#pragma unroll
-    for (int b = 0; b < 2; b++) {
-        const uint32_t sb = (sc2 >> (8 * b)) & 0xFFu, e = (sb >> 3) & 15u, m = sb & 7u;
-        // E4M3 scale = f * 2^E: subnormal f = m, E = -9; normal f = 8 + m, E = e - 10
-        p2[b] = exp2i(e == 0 ? -9 : (int)e - 10);
-        fct[b] = sb == 0x7Fu ? (_Float16)__builtin_nanf("") : (_Float16)(float)(e == 0 ? m : 8u + m);
-    }
+    const h2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc2, 1.0f, false);   // {scale 0, scale 1}
     const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
 #pragma unroll
     for (int q = 0; q < 4; q++) {                    // 16-byte output chunk q: code bytes 4q .. 4q+3
-        const int b = q / 2;                         // bytes 0-7: block 0, bytes 8-15: block 1
-        const h2 f2 = {fct[b], fct[b]};
-        h2 v[4];
-        v[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], p2[b], 0) * f2;
-        v[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], p2[b], 1) * f2;
-        v[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], p2[b], 2) * f2;
-        v[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], p2[b], 3) * f2;
-        const h8 out = {v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
-        *(h8*)(tile + nv_swz(row, 4 * half + q)) = out;
+        const h2 f2 = q < 2 ? h2{sc[0], sc[0]} : h2{sc[1], sc[1]};   // bytes 0-7: block 0, 8-15: block 1
+        const h2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], 1.0f, 0) * f2;
+        const h2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], 1.0f, 1) * f2;
+        const h2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], 1.0f, 2) * f2;
+        const h2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], 1.0f, 3) * f2;
+        *(h8*)(tile + nv_swz(row, 4 * half + q)) = h8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
     }
 }
 
@@ -442,28 +440,50 @@ void k_nv_gemm(NvGemmJob g, int tiles_m, int tiles_n)
     gload(0);
     dq_write(0);
     if (nst > 1) gload(1);
-    __syncthreads();
+    lds_barrier();
+    // fragments of k-step ks of buffer `buf`: A tiles 0..3, B tiles 0..3 of the wave
+    struct Frag { h8 a[4], b[4]; };
+    auto rd_frags = [&](Frag& f, int buf, int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            f.a[i] = *(const h8*)(lA[buf] + nv_swz(wm * 128 + i * 32 + l32, 2 * ks + h));
+            f.b[i] = *(const h8*)(lB[buf] + nv_swz(wn * 128 + i * 32 + l32, 2 * ks + h));
+        }
+    };
+    auto mmas = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    };
+    // each k-step's fragments are read while the previous k-step's 16 MFMAs
+    // run (two register sets); the fences keep the reads ahead of the MFMAs
+    Frag F0, F1;
     for (int s = 0; s < nst; s++) {
         const int cur = s & 1;
-#pragma unroll
-        for (int ks = 0; ks < NBK / 16; ks++) {
-            h8 a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                a[i] = *(const h8*)(lA[cur] + nv_swz(wm * 128 + i * 32 + l32, 2 * ks + h));
-                b[i] = *(const h8*)(lB[cur] + nv_swz(wn * 128 + i * 32 + l32, 2 * ks + h));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
+        rd_frags(F0, cur, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        rd_frags(F1, cur, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mmas(F0);
+        __builtin_amdgcn_sched_barrier(0);
+        rd_frags(F0, cur, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mmas(F1);
+        __builtin_amdgcn_sched_barrier(0);
+        rd_frags(F1, cur, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        mmas(F0);
+        __builtin_amdgcn_sched_barrier(0);
+        mmas(F1);
+        __builtin_amdgcn_sched_barrier(0);
         if (s + 1 < nst) {
             dq_write(cur ^ 1);                       // stage s+1 into the buffer stage s-1 used
             if (s + 2 < nst) gload(s + 2);
         }
-        __syncthreads();
+        // LDS hand-off only: the loads of stage s+2 stay in flight across it
+        lds_barrier();
     }
 
     // epilogue: alpha and the two second-level scales once per output
