@@ -128,6 +128,33 @@ def setup_moss(args):
     return step, info
 
 
+def setup_c1(args):
+    """MXFP8 GEMM 256^3 (fp32 A, B ~ N(0, 1); E4M3 row copy of A, column copy
+    of B, round to nearest; bf16 out): the smallest configuration, dominated
+    by launch and single-tile latency."""
+    w = I.make("mxfp8_gemm_256")
+    A, B = to_dev(w.tensors["A"]), to_dev(w.tensors["B"])
+    M, K = A.shape
+    N = B.shape[1]
+    cfg = mx.qconfig("e4m3")
+    qa, sa, _ = mx.mx_quantize(A, mx.MX_AXIS_ROW, cfg)
+    qb, sb, _ = mx.mx_quantize(B, mx.MX_AXIS_COL, cfg)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(t):
+        t.run("quant_A", lambda: mx.mx_quantize(A, mx.MX_AXIS_ROW, cfg, qa, sa))
+        t.run("quant_B", lambda: mx.mx_quantize(B, mx.MX_AXIS_COL, cfg, qb, sb))
+        t.run("gemm", lambda: mx.mx_gemm(qa, sa, None, "e4m3", qb, sb, None, "e4m3", M, N, K,
+                                         out_dtype=mx.MX_OUT_BF16, c=C))
+
+    qbytes = lambda R, Cc: 4 * R * Cc + R * Cc + R * Cc // 32      # fp32 in, E4M3 codes + scales out
+    info = dict(flops=2.0 * M * N * K, qbytes={"quant_A": qbytes(M, K), "quant_B": qbytes(K, N)},
+                gemm_kernel="gemm", mfma="fp8",
+                config={"workload": "mxfp8_gemm_256", "M": M, "N": N, "K": K, "elem": "e4m3",
+                        "scales": "e8m0 1x32", "out": "bf16"}, host=w.tensors)
+    return step, info
+
+
 def setup_dual(args):
     w = I.make("dual_layout_16384x14336")
     X = to_dev(w.tensors["X"])
@@ -380,7 +407,7 @@ def setup_copy(args):
     return step, info
 
 
-WORKLOADS = {"moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4, "llama": setup_llama,
+WORKLOADS = {"c1": setup_c1, "moss": setup_moss, "dual": setup_dual, "fp4": setup_fp4, "llama": setup_llama,
              "copy": setup_copy, "autoscale": setup_autoscale, "mxout": setup_mxout, "coat": setup_coat,
              "nvfp_global": setup_nvfp_global, "nvfp_local": setup_nvfp_local}
 

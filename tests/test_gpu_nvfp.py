@@ -206,3 +206,32 @@ def test_full_llama3_8b_gate(local):
     log(f"llama gate local={local}: {ii.size} sampled outputs, max err / stated tolerance {r[0]:.3g}")
     record({"test": "nvfp_gemm", "case": f"llama3_8b_gate local={local}", "sampled": int(ii.size),
             "max_err_over_stated": r[0], "inside_stated": r[1]})
+
+
+def test_gemm_dequantizes_every_code_exactly():
+    """The GEMM's in-loop dequantization is exact for every E4M3 block scale
+    (subnormals and NaN included) times every E2M1 code: hand-built operands
+    with A row i using scale code i on all its blocks and code k % 16 at
+    position k, against a B that selects one position per column (code 1.0
+    under scale 1.0).  Each output is then a single product, which the f16
+    matrix cores and the fp32 accumulator carry without rounding, so C must
+    equal e2m1(k % 16) * e4m3(i) bit for bit (NaN for the NaN scale code)."""
+    M, N, K = 128, 64, 64
+    kk = np.arange(K)
+    codes = np.tile((kk % 16).astype(np.uint8), (M, 1))                       # [M][K] nibbles
+    qa = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)            # element 2j low nibble
+    sa = np.repeat(np.arange(M, dtype=np.uint8)[:, None], K // 16, axis=1)    # scale code i on row i
+    bc = np.zeros((N, K), np.uint8)
+    bc[np.arange(N), np.arange(N)] = 0x2                                      # E2M1 1.0 at k = j
+    qb = (bc[:, 0::2] | (bc[:, 1::2] << 4)).astype(np.uint8)
+    sb = np.full((N, K // 16), 0x38, np.uint8)                                # E4M3 1.0
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    c = mx.mx_gemm_nvfp(dv(qa), dv(sa), one, False, dv(qb), dv(sb), one, False, M, N, K, 1.0, mx.MX_OUT_F32)
+    got = c.cpu().numpy()
+    e2m1 = np.array([O.decode("e2m1", v) for v in range(16)])
+    e4m3 = np.array([O.decode("e4m3", v) for v in range(128)])
+    # exact in fp32; a signed zero product sums to +0 with the accumulator's +0
+    ref = (e4m3[:, None] * e2m1[kk[:N] % 16][None, :]).astype(np.float32) + np.float32(0.0)
+    assert_same_f32(got, ref)
+    assert np.isnan(got[0x7F]).all() and (got[0] == 0).all()
