@@ -300,6 +300,227 @@ __global__ __launch_bounds__(256) void k_nv_quant_col(const void* x, int64_t row
     }
 }
 
+// ---------------------------------------------------------------------------
+// k_nv_quant_local: the CTA-local route in one pass.  One 1024-thread
+// workgroup per panel of 32 stored rows of a bf16 source whose blocked
+// length L is at most 4096: the panel (32 x L elements, at most 256 KiB) is
+// read once into registers (16 bytes x 16 per thread), its amax reduced
+// inside the workgroup into the panel's scale, and its blocks quantized from
+// the registers.  No other workgroup is involved, so there is no second
+// kernel and no second read of the source.
+//   row copy (panel = source rows 32p..): thread chunk c = tid + 1024 i is
+//     8 consecutive elements of panel row c / (L / 8); the two threads
+//     holding a 16-block (adjacent lanes) exchange their maxima by a lane
+//     shuffle and each writes its 8 codes (4 bytes).
+//   column copy (panel = source columns 32p..): thread tid holds row block
+//     tid / 4 (16 source rows) x column group tid % 4 (8 columns), i.e. 8
+//     whole column blocks; four adjacent lanes read a row's 64-byte panel
+//     segment, and 16 lanes write 128 contiguous code bytes of a column.
+// ---------------------------------------------------------------------------
+constexpr int NV_FUSED_THREADS = 1024, NV_FUSED_MAXL = 4096;
+
+// E4M3 block-scale byte and the code reciprocal of a block whose amax key
+// is `key` under second-level scale s (the arithmetic of nv_block); a zero
+// scale returns r = 0 (signed-zero codes), a NaN block or domain 0x7F
+__device__ __forceinline__ uint32_t nv_block_scale(uint32_t key, float s, float& r)
+{
+    r = 0.0f;
+    if (key >= 0x7F800000u || s != s) return 0x7Fu;
+    const float den = 6.0f * s;
+    const float bv = __uint_as_float(key) / den;
+    const uint32_t sb = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fmax<E4M3>(bv), 0.0f, 0, false) & 0x7Fu;
+    const float ds = e4m3_value(sb);
+    if (ds != 0.0f) {
+        const float d = ds * s;
+        r = 1.0f / d;
+    }
+    return sb;
+}
+
+// 8 codes of 8 bf16 values (packed in 4 dwords) under a block scale: r = 0
+// gives the signed zeros, sb = 0x7F zero codes
+__device__ __forceinline__ uint32_t nv_encode8(const uint32_t* w, uint32_t sb, float r)
+{
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        y[2 * k] = __uint_as_float(w[k] << 16);
+        y[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+    if (sb == 0x7Fu) return 0u;
+    if (r == 0.0f) {
+        uint32_t z = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) z |= (__float_as_uint(y[i]) >> 31) << (4 * i + 3);
+        return z;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) y[i] = clamp_fmax<E2M1>(y[i] * r);
+    return cvt8_fp4(y);
+}
+
+// |max| key of 8 bf16 values packed in 4 dwords (NaN above Inf above finite)
+__device__ __forceinline__ uint32_t bf16x8_key(const uint32_t* w)
+{
+    uint32_t key = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) key = max(key, max((w[k] & 0x7FFFu) << 16, w[k] & 0x7FFF0000u));
+    return key;
+}
+
+// ---------------------------------------------------------------------------
+// k_nv_quant_local: the CTA-local route in one pass.  One 1024-thread
+// workgroup per panel of 32 stored rows of a bf16 source whose blocked
+// length L is at most 4096: the panel (32 x L elements, at most 256 KiB) is
+// read once into registers (16 bytes x 16 per thread), its amax reduced
+// inside the workgroup into the panel's scale, and its blocks quantized from
+// the registers.  No other workgroup is involved, so there is no second
+// kernel and no second read of the source.
+//   row copy (panel = source rows 32p..): thread chunk c = tid + 1024 i is
+//     8 consecutive elements of panel row c / (L / 8); the two threads
+//     holding a 16-block (adjacent lanes) exchange their maxima by a lane
+//     shuffle and each writes its 8 codes (4 bytes).
+//   column copy (panel = source columns 32p..): thread tid holds row block
+//     tid / 4 (16 source rows) x column group tid % 4 (8 columns), i.e. 8
+//     whole column blocks; four adjacent lanes read a row's 64-byte panel
+//     segment, and 16 lanes write 128 contiguous code bytes of a column.
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t nv_rsrc(const void* base, int64_t bytes)
+{
+    bytes = bytes < 0 ? 0 : bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
+template <bool ROW>
+__global__ __launch_bounds__(1024) void k_nv_quant_local(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                                         int64_t npanels, float* ts, uint8_t* q, uint8_t* s16)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t L = ROW ? cols : rows, SR = ROW ? rows : cols, nb = L / 16;
+    const int cpr = (int)(L / 8);                    // row copy: 8-element chunks per panel row
+    const int nrb = (int)(L / 16);                   // column copy: 16-row blocks
+    __shared__ uint32_t red[16];
+    __shared__ float panel_s;
+    for (int64_t p = blockIdx.x; p < npanels; p += gridDim.x) {
+        // the thread index passes through an empty asm per panel, so that the
+        // 16 load offsets are recomputed here rather than hoisted out of the
+        // panel loop (where they would stay live, and spill, beside the data)
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int64_t sr0 = p * NV_PANEL;
+        const int np = (int)min((int64_t)NV_PANEL, SR - sr0);      // stored rows in this panel
+        // buffer views of the panel: 32-bit offsets; source rows / stored rows
+        // past the panel read as zero and their stores are dropped
+        const auto rx = ROW ? nv_rsrc(x + sr0 * ld, ((int64_t)(np - 1) * ld + L) * 2)
+                            : nv_rsrc(x + sr0, ((L - 1) * ld + (SR - sr0)) * 2);
+        const auto rq = nv_rsrc(q + sr0 * (L / 2), (int64_t)np * (L / 2));
+        const auto rs = nv_rsrc(s16 + sr0 * nb, (int64_t)np * nb);
+        uint4 v[16];
+        if (ROW) {
+            // thread: panel row tid / 32, chunks (tid % 32) + 32 i
+            const int r = tid >> 5;
+            const uint32_t base = (uint32_t)((int64_t)r * ld * 2) + (uint32_t)((tid & 31) * 16);
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                // chunks past the row (L < 4096) get an offset at or above 2^31
+                const uint32_t off = base + (uint32_t)(512 * i) + ((tid & 31) + 32 * i < cpr ? 0u : 0x80000000u);
+                v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+            }
+        } else {
+            // unit: row block tid / 4, column group tid % 4 -- four adjacent
+            // lanes read one row's 64-byte panel segment
+            const int rb = tid >> 2, cg = tid & 3;
+            // a unit past the panel (SR % 8 == 0 here: whole chunks) gets an
+            // offset at or above 2^31, beyond the view's range (below 2^31)
+            const uint32_t base = (uint32_t)(((int64_t)rb * 16 * ld + 8 * cg) * 2) +
+                                  ((rb < nrb && 8 * cg < np) ? 0u : 0x80000000u);
+            const uint32_t rstep = (uint32_t)(ld * 2);
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, base + (uint32_t)i * rstep, 0, 0));
+        }
+        // all 16 loads in flight before the first use
+        __builtin_amdgcn_sched_barrier(0);
+        // panel amax
+        uint32_t key = 0;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            key = max(key, bf16x8_key(w));
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
+        if (lane == 0) red[wave] = key;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t k2 = red[0];
+            for (int i = 1; i < 16; i++) k2 = max(k2, red[i]);
+            panel_s = domain_scale(k2);
+            ts[p] = panel_s;
+        }
+        __syncthreads();
+        const float s = panel_s;
+        // (likewise for the store offsets, and for the held data: nothing of
+        // the quantization is computed before the panel's scale is known)
+        asm volatile("" : "+v"(tid));
+#pragma unroll
+        for (int i = 0; i < 16; i++) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+        if (ROW) {
+            const int r = tid >> 5;
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                // chunks cc and cc ^ 1 (adjacent lanes) form one 16-block; every
+                // lane takes part in the shuffle
+                const int cc = (tid & 31) + 32 * i;
+                const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+                const uint32_t own = bf16x8_key(w);
+                const uint32_t bkey = max(own, (uint32_t)__shfl_xor((int)own, 1));
+                float rc;
+                const uint32_t sb = nv_block_scale(bkey, s, rc);
+                const uint32_t codes = nv_encode8(w, sb, rc);
+                if (cc < cpr) {
+                    const uint32_t qo = (uint32_t)(r * (L / 2) + (cc >> 1) * 8 + (cc & 1) * 4);
+                    __builtin_amdgcn_raw_buffer_store_b32(codes, rq, qo, 0, 0);
+                    if ((cc & 1) == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rs, (uint32_t)(r * nb + (cc >> 1)), 0, 0);
+                }
+                // one chunk at a time: keeps the scheduler from overlapping the
+                // chunks' temporaries with the 64 registers of held data
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            const int rb = tid >> 2, cg = tid & 3;
+            if (rb < nrb) {
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    // column k of the 16 rows, as two runs of 8 packed bf16
+                    uint32_t lo[4], hi[4];
+#pragma unroll
+                    for (int i = 0; i < 8; i += 2) {
+                        const uint32_t a0 = k < 2 ? v[i].x : k < 4 ? v[i].y : k < 6 ? v[i].z : v[i].w;
+                        const uint32_t a1 = k < 2 ? v[i + 1].x : k < 4 ? v[i + 1].y : k < 6 ? v[i + 1].z : v[i + 1].w;
+                        const uint32_t b0 = k < 2 ? v[8 + i].x : k < 4 ? v[8 + i].y : k < 6 ? v[8 + i].z : v[8 + i].w;
+                        const uint32_t b1 = k < 2 ? v[9 + i].x : k < 4 ? v[9 + i].y : k < 6 ? v[9 + i].z : v[9 + i].w;
+                        // element k of a dword pair: low halves for even k, high for odd
+                        lo[i / 2] = (k & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u) : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+                        hi[i / 2] = (k & 1) ? __builtin_amdgcn_perm(b1, b0, 0x07060302u) : __builtin_amdgcn_perm(b1, b0, 0x05040100u);
+                    }
+                    const uint32_t bkey = max(bf16x8_key(lo), bf16x8_key(hi));
+                    float rc;
+                    const uint32_t sb = nv_block_scale(bkey, s, rc);
+                    const uint32_t c0 = nv_encode8(lo, sb, rc), c1 = nv_encode8(hi, sb, rc);
+                    const int srl = 8 * cg + k;              // stored row within the panel
+                    const uint32_t qo = (uint32_t)(srl * (L / 2) + rb * 8);
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2v{c0, c1}, rq, qo, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rs, (uint32_t)(srl * nb + rb), 0, 0);
+                }
+            }
+        }
+        __syncthreads();                             // panel_s and red are reused by the next panel
+    }
+}
+
 // dequantize: one thread per block; x_hat = (code * decode(sb)) * s, the
 // first product exact
 template <bool ROW, int OUTT>
@@ -520,10 +741,17 @@ unsigned nv_grid(int64_t items)
 template <int SRC, bool ROW>
 hipError_t launch_nv_quant(const NvQuantJob& j, hipStream_t st)
 {
-    const int64_t SR = ROW ? j.rows : j.cols;
+    const int64_t SR = ROW ? j.rows : j.cols, L = ROW ? j.cols : j.rows;
     const int64_t npanels = (SR + NV_PANEL - 1) / NV_PANEL;
     const int64_t es = SRC == SRC_BF16 ? 2 : 4;
     const bool vec = ((uintptr_t)j.x % 16) == 0 && (j.ld * es) % 16 == 0 && j.cols % 8 == 0;
+    // (source offsets within a panel stay below 2^31 bytes)
+    if (SRC == SRC_BF16 && j.local && vec && L <= NV_FUSED_MAXL && (ROW ? 32 : L) * j.ld * es < ((int64_t)1 << 31)) {
+        // CTA-local, one pass: the panel fits one workgroup's registers
+        k_nv_quant_local<ROW><<<(unsigned)std::min<int64_t>(npanels, 65535), NV_FUSED_THREADS, 0, st>>>(
+            (const uint16_t*)j.x, j.rows, j.cols, j.ld, npanels, j.ts, j.q, j.s16);
+        return hipGetLastError();
+    }
     // amax partials: about 2048 workgroups; parked in the code array, which
     // the quantize kernel overwrites afterwards (npanels * G * 4 bytes is at
     // most rows * cols / 4, the array holds rows * cols / 2)

@@ -116,6 +116,22 @@ def test_single_row_and_block():
     _compare_copy(rng.standard_normal((1, 16)).astype(np.float32), mx.MX_AXIS_ROW, True, "1x16 row")
     _compare_copy(rng.standard_normal((16, 1)).astype(np.float32), mx.MX_AXIS_COL, False, "16x1 col")
     _compare_copy(rng.standard_normal((16, 3)).astype(np.float32), mx.MX_AXIS_COL, True, "16x3 col")
+    # bf16, CTA-local: the one-pass kernel (one stored row; one 8-column panel)
+    _compare_copy(I.to_bf16_bits(rng.standard_normal((1, 16)).astype(np.float32)), mx.MX_AXIS_ROW, True, "1x16 bf16")
+    _compare_copy(I.to_bf16_bits(rng.standard_normal((16, 8)).astype(np.float32)), mx.MX_AXIS_COL, True, "16x8 bf16")
+
+
+@pytest.mark.parametrize("axis", [mx.MX_AXIS_ROW, mx.MX_AXIS_COL])
+def test_local_one_pass_shapes(axis):
+    """The one-pass CTA-local kernel (bf16, blocked length <= 4096) at its
+    limit and with ragged panels: L = 4096 with 40 stored rows, and a short
+    L = 48 (only 6 chunks of a 32-lane row group in use)."""
+    rng = np.random.default_rng(60 + axis)
+    for SR, L in ((40, 4096), (72, 48)):
+        rows, cols = (SR, L) if axis == mx.MX_AXIS_ROW else (L, SR)
+        x = _source(rng, rows, cols, "bf16")
+        log(f"one-pass local axis={axis} {rows}x{cols}")
+        _compare_copy(x, axis, True, f"one-pass axis={axis} {rows}x{cols}")
 
 
 def test_invalid_arguments():
