@@ -25,10 +25,15 @@
 // transcendental's approximation.  Accuracy: a few fp32 ulps for log2 and
 // exp2, about 1e-6 relative for the powers, far below an FP8 step.
 //
-// Bound by HBM: 4 bytes read and 1 written per element, 8 bytes of
-// parameters per group.  One thread handles 4 consecutive elements
-// (16-byte loads, 4-byte code stores); the G/4 threads of a group reduce
-// amax and amin with lane shuffles inside their wave.
+// 4 bytes read and 1 written per element, 8 bytes of parameters per group;
+// the exact fp32 sequence makes the kernels bound by VALU work.  Two ways of
+// doing less of it while computing the same bits: the quantizer's |x|/amax
+// uses the reciprocal-plus-residual division (TensorDiv: the IEEE quotient,
+// with the IEEE division as fallback), and the dequantizer looks log2 of
+// each decoded magnitude up in a per-workgroup table, since it depends on
+// the code alone.  One thread handles 4 consecutive elements (16-byte loads,
+// 4-byte code stores); the G/4 threads of a group reduce amax and amin with
+// lane shuffles inside their wave.
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -156,10 +161,21 @@ __global__ __launch_bounds__(256) void k_optstate_quant(const float4* __restrict
             const float r = amax / amin;
             const float k = r > 1.0f ? Range<FMT>::log2r / log2_fixed(r) : 1.0f;
             const float xs[4] = {v.x, v.y, v.z, v.w};
+            // u = |x| / amax, the IEEE quotient (quotients are at most 1; an
+            // element far below amax takes the IEEE division)
+            const TensorDiv d = make_div(amax);
+            uint32_t lo = ~0u;
+            float u[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) u[i] = div_fast(a[i], d, lo);
+            if (!d.fast || lo < d.lo_key) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) u[i] = a[i] / amax;
+            }
             float y[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const float e = pow_fixed(a[i] / amax, k) * Fmt<FMT>::fmax;
+                const float e = pow_fixed(u[i], k) * Fmt<FMT>::fmax;
                 y[i] = clamp_fmax<FMT>(__builtin_copysignf(e, xs[i]));
             }
             codes = cvt4_fp8<FMT>(y[0], y[1], y[2], y[3]);
@@ -176,6 +192,12 @@ __global__ __launch_bounds__(256) void k_optstate_dequant(const uint32_t* __rest
 {
 #pragma clang fp contract(off)
     constexpr int T = G / 4;
+    // log2(|decode(c)| / Fmax) for the 128 magnitudes, in the same fixed
+    // sequence the per-element form evaluates (code 0, whose power is 0, is
+    // never looked up)
+    __shared__ float lg[128];
+    for (int c = threadIdx.x; c < 128; c += 256) lg[c] = log2_fixed(fabsf(decode8<FMT>((uint32_t)c)) / Fmt<FMT>::fmax);
+    __syncthreads();
     for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < nthreads; t += (int64_t)gridDim.x * 256) {
         const uint32_t c4 = q[t];
         const int64_t g = t / T;
@@ -184,10 +206,12 @@ __global__ __launch_bounds__(256) void k_optstate_dequant(const uint32_t* __rest
         float o[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const uint32_t c = (c4 >> (8 * i)) & 0xFFu;
-            const float v = decode8<FMT>(c);
-            float m = amax * pow_fixed(fabsf(v) / Fmt<FMT>::fmax, kinv);
-            if (v != v || amax != amax || k != k) m = __builtin_nanf("");
+            const uint32_t c = (c4 >> (8 * i)) & 0xFFu, c7 = c & 0x7Fu;
+            // NaN codes: E4M3 0x7F; E5M2 0x7D-0x7F (0x7C is Inf)
+            const bool nan_code = FMT == E4M3 ? c7 == 0x7Fu : c7 > 0x7Cu;
+            const float pw = c7 == 0 ? 0.0f : exp2_fixed(kinv * lg[c7]);
+            float m = amax * pw;
+            if (nan_code || amax != amax || k != k) m = __builtin_nanf("");
             o[i] = (c & 0x80u) ? -m : m;
         }
         out[t] = make_float4(o[0], o[1], o[2], o[3]);

@@ -75,53 +75,6 @@ __device__ __forceinline__ float tensor_scale_from_key(uint32_t key)
     return __uint_as_float(key) / Fmt<FMT>::fmax;
 }
 
-// x / s_t rounded to nearest even, with s_t fixed for the whole tensor.  The
-// reciprocal r = RN(1/s_t) is formed once; q = RN(x r) refined by one exact
-// residual step q' = RN(q + RN(x - q s_t) r) equals the IEEE quotient.  This
-// is Markstein's correction theorem (P. Markstein, IBM J. Res. Dev. 34(1),
-// 1990; Theorem 8.10 of Muller et al., Handbook of Floating-Point
-// Arithmetic): if r is within half an ulp of 1/s_t (here r = RN(1/s_t))
-// and q within one ulp of x/s_t (q = RN(x r) is: the reciprocal's half-ulp
-// error and the product's rounding stay below one ulp), the residual
-// x - q s_t is exactly representable and one FMA returns RN(x/s_t) --
-// provided nothing underflows or overflows along the way.  The range checks
-// keep away from those cases: the kernels require |x|, |q'| >= 2^-96 and
-// |q'| <= 2^17 (the range over which the identity was also checked
-// exhaustively, every fp32 x against divisors with adversarial
-// significands).  Per block they check |x| >= T = max(2^-96, 2^-95 |s_t|)
-// for every nonzero x (which implies |q'| >= 2^-96) and |q'| <= 2^17 on the
-// block's largest quotient; a block that fails takes the IEEE division.
-// Zeros keep the sign of x r; a non-finite x makes the block non-finite
-// either way.
-struct TensorDiv {
-    float s, r;
-    uint32_t lo_key;    // (bits(T) << 1) - 1
-    bool fast;          // s and 1/s are normal fp32 numbers
-};
-
-__device__ __forceinline__ TensorDiv make_div(float s)
-{
-    TensorDiv d;
-    const float as = fabsf(s);
-    d.s = s;
-    d.r = 1.0f / s;
-    d.fast = as > 0x1p-125f && as < 0x1p125f;
-    const float t = d.fast ? fmaxf(0x1p-96f, 0x1p-95f * as) : 1.0f;
-    d.lo_key = (__float_as_uint(t) << 1) - 1u;
-    return d;
-}
-
-// fast quotient; `lo` tracks min((bits(x) << 1) - 1), whose value is below
-// lo_key exactly when some nonzero |x| < T
-__device__ __forceinline__ float div_fast(float x, const TensorDiv& d, uint32_t& lo)
-{
-    const float q0 = x * d.r;
-    const float rem = __builtin_fmaf(-q0, d.s, x);
-    const float q1 = __builtin_fmaf(rem, d.r, q0);
-    lo = min(lo, (__float_as_uint(x) << 1) - 1u);
-    return __builtin_copysignf(q1, q0);
-}
-
 // The 32 values of one block ready for the block scale: source values from
 // elem(i), divided by s_t (two-level) and transformed (Hadamard).  Returns the
 // block's |max| key.
