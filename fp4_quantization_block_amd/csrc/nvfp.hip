@@ -319,21 +319,24 @@ __global__ __launch_bounds__(256) void k_nv_quant_col(const void* x, int64_t row
 // ---------------------------------------------------------------------------
 constexpr int NV_FUSED_THREADS = 1024, NV_FUSED_MAXL = 4096;
 
-// E4M3 block-scale byte and the code reciprocal of a block whose amax key
-// is `key` under second-level scale s (the arithmetic of nv_block); a zero
-// scale returns r = 0 (signed-zero codes), a NaN block or domain 0x7F
-__device__ __forceinline__ uint32_t nv_block_scale(uint32_t key, float s, float& r)
+// E4M3 block-scale byte and the code reciprocal r of a block whose amax key
+// is `key` under the panel's second-level scale s -- the arithmetic of
+// nv_block (a zero scale gives r = 0: signed-zero codes; a NaN block or
+// domain 0x7F) with the panel's divisions hoisted: amax / (6 s) through
+// the reciprocal-plus-residual division (the IEEE quotient; IEEE division
+// outside its range), and RN(1 / RN(decode(sb) s)) from a table of the 127
+// finite scale codes -- the same values, computed once per panel
+__device__ __forceinline__ uint32_t nv_block_scale_tab(uint32_t key, float s, const TensorDiv& dden,
+                                                       const float* rtab, float& r)
 {
     r = 0.0f;
     if (key >= 0x7F800000u || s != s) return 0x7Fu;
-    const float den = 6.0f * s;
-    const float bv = __uint_as_float(key) / den;
+    const float a = __uint_as_float(key);
+    uint32_t lo = ~0u;
+    float bv = div_fast(a, dden, lo);
+    if (!dden.fast || lo < dden.lo_key || bv > 0x1p17f) bv = a / dden.s;
     const uint32_t sb = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fmax<E4M3>(bv), 0.0f, 0, false) & 0x7Fu;
-    const float ds = e4m3_value(sb);
-    if (ds != 0.0f) {
-        const float d = ds * s;
-        r = 1.0f / d;
-    }
+    r = rtab[sb];
     return sb;
 }
 
@@ -403,7 +406,16 @@ __global__ __launch_bounds__(1024) void k_nv_quant_local(const uint16_t* x, int6
     const int nrb = (int)(L / 16);                   // column copy: 16-row blocks
     __shared__ uint32_t red[16];
     __shared__ float panel_s;
-    for (int64_t p = blockIdx.x; p < npanels; p += gridDim.x) {
+    __shared__ float rtab[128];                      // RN(1 / RN(e4m3(c) s)), 0 for a zero scale
+    for (int64_t w = blockIdx.x; w < npanels; w += gridDim.x) {
+        // Column copy: a panel's rows are 64-byte halves of 128-byte lines whose
+        // other halves belong to the neighbouring panels.  Workgroups are dealt
+        // to the 8 XCDs round-robin; giving each XCD a contiguous range of
+        // panels (when the grid is one panel per workgroup and divides by 8)
+        // lets neighbours share their lines in one L2 instead of fetching them
+        // twice from HBM.
+        const int64_t p = (!ROW && gridDim.x == npanels && (npanels & 7) == 0)
+                              ? (w & 7) * (npanels >> 3) + (w >> 3) : w;
         // the thread index passes through an empty asm per panel, so that the
         // 16 load offsets are recomputed here rather than hoisted out of the
         // panel loop (where they would stay live, and spill, beside the data)
@@ -462,6 +474,12 @@ __global__ __launch_bounds__(1024) void k_nv_quant_local(const uint16_t* x, int6
         }
         __syncthreads();
         const float s = panel_s;
+        if (tid < 128) {
+            const float ds = e4m3_value((uint32_t)tid);
+            rtab[tid] = ds == 0.0f ? 0.0f : 1.0f / (ds * s);
+        }
+        const TensorDiv dden = make_div(6.0f * s);
+        __syncthreads();
         // (likewise for the store offsets, and for the held data: nothing of
         // the quantization is computed before the panel's scale is known)
         asm volatile("" : "+v"(tid));
@@ -478,7 +496,7 @@ __global__ __launch_bounds__(1024) void k_nv_quant_local(const uint16_t* x, int6
                 const uint32_t own = bf16x8_key(w);
                 const uint32_t bkey = max(own, (uint32_t)__shfl_xor((int)own, 1));
                 float rc;
-                const uint32_t sb = nv_block_scale(bkey, s, rc);
+                const uint32_t sb = nv_block_scale_tab(bkey, s, dden, rtab, rc);
                 const uint32_t codes = nv_encode8(w, sb, rc);
                 if (cc < cpr) {
                     const uint32_t qo = (uint32_t)(r * (L / 2) + (cc >> 1) * 8 + (cc & 1) * 4);
@@ -508,7 +526,7 @@ __global__ __launch_bounds__(1024) void k_nv_quant_local(const uint16_t* x, int6
                     }
                     const uint32_t bkey = max(bf16x8_key(lo), bf16x8_key(hi));
                     float rc;
-                    const uint32_t sb = nv_block_scale(bkey, s, rc);
+                    const uint32_t sb = nv_block_scale_tab(bkey, s, dden, rtab, rc);
                     const uint32_t c0 = nv_encode8(lo, sb, rc), c1 = nv_encode8(hi, sb, rc);
                     const int srl = 8 * cg + k;              // stored row within the panel
                     const uint32_t qo = (uint32_t)(srl * (L / 2) + rb * 8);
