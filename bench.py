@@ -45,22 +45,34 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0,   # dense scaled MFMA
 # commands are in profiles/.  Keyed by the SHA-256 of the kernel's source
 # file at measurement time: a changed kernel reports null until re-measured.
 MEASURED_TRAFFIC = {
-    "moss": {"source": "gemm.hip", "sha256": "4e5111340904f308",
-             "fetch_kib": 50805.1, "write_kib": 32786.2},
+    "moss": {"source": "gemm.hip", "sha256": "67670a25d4abdb9c",
+             "fetch_kib": 50812.5, "write_kib": 32794.6},
     # the GEMM launches of one step together (six GEMMs, the last one's final
     # partial round of tiles as a second launch; the roofline's unit here)
     "llama": {"source": "gemm.hip", "sha256": "67670a25d4abdb9c",
               "fetch_kib": 3202689.4, "write_kib": 1164633.2},
-    "fp4": {"source": "gemm.hip", "sha256": "4e5111340904f308",
-            "fetch_kib": 183584.7, "write_kib": 49154.8},
-    "mxout": {"source": "gemm.hip", "sha256": "4e5111340904f308",
-              "fetch_kib": 50868.1, "write_kib": 18782.1},
-    # the fused amax pass of the prediction (k_amax_partial2)
-    "autoscale": {"source": "quant.hip", "sha256": "44988e745806c8be",
-                  "fetch_kib": 32811.5, "write_kib": 32.0},
+    # the GEMM call's two launches (a full round of 256x256 tiles, then the
+    # last tile rows as 256x128 half tiles)
+    "fp4": {"source": "gemm.hip", "sha256": "67670a25d4abdb9c",
+            "fetch_kib": 174302.8, "write_kib": 49157.1},
+    "mxout": {"source": "gemm.hip", "sha256": "67670a25d4abdb9c",
+              "fetch_kib": 50868.4, "write_kib": 20211.6},
+    "c1": {"source": "gemm.hip", "sha256": "67670a25d4abdb9c",
+           "fetch_kib": 81.7, "write_kib": 128.0},
+    # the prediction call (k_amax_partial2 + k_predict_scale)
+    "autoscale": {"source": "quant.hip", "sha256": "b18754e66b4322bd",
+                  "fetch_kib": 32815.3, "write_kib": 32.1},
     # the dual-layout quantizer (k_quant_tile_dma)
-    "dual": {"source": "quant.hip", "sha256": "44988e745806c8be",
-             "fetch_kib": 229542.2, "write_kib": 496738.2},
+    "dual": {"source": "quant.hip", "sha256": "b18754e66b4322bd",
+             "fetch_kib": 229549.2, "write_kib": 496622.1},
+    # k_nv_gemm
+    "nvfp_global": {"source": "nvfp.hip", "sha256": "12fa371ea1a3a812",
+                    "fetch_kib": 195547.2, "write_kib": 229500.6},
+    "nvfp_local": {"source": "nvfp.hip", "sha256": "12fa371ea1a3a812",
+                   "fetch_kib": 195549.9, "write_kib": 229530.2},
+    # k_optstate_dequant of the first moment
+    "coat": {"source": "optstate.hip", "sha256": "a8142a89099e70dc",
+             "fetch_kib": 71709.8, "write_kib": 458752.0},
 }
 
 
