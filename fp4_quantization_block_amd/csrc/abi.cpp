@@ -321,6 +321,12 @@ mx_status check_gemm_operands(const void* qa, const uint8_t* sa, const float* ta
     if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(MX_ERR_INVALID_ARG, "unknown element format");
     if (M <= 0 || N <= 0 || K <= 0) return fail(MX_ERR_INVALID_ARG, "M, N, K must be > 0");
     if (K % 32 != 0) return fail(MX_ERR_INVALID_ARG, "K must be a multiple of 32");
+    // the kernels address a 256-row operand tile with 32-bit offsets from its
+    // first row, and number their workgroups with 32-bit integers
+    if (K > (int64_t)1 << 23) return fail(MX_ERR_INVALID_ARG, "K must be <= 2^23");
+    if (M > ((int64_t)1 << 31) - 256 || N > ((int64_t)1 << 31) - 256) return fail(MX_ERR_INVALID_ARG, "M and N must be < 2^31 - 256");
+    if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t)1 << 31)
+        return fail(MX_ERR_INVALID_ARG, "M x N must be fewer than 2^31 output tiles of 256 x 256");
     if (hadamard_k != 0 && hadamard_k != 1) return fail(MX_ERR_INVALID_ARG, "hadamard_k must be 0 or 1");
     if (elem_bits(fa) != elem_bits(fb)) return fail(MX_ERR_UNSUPPORTED, "mixed FP8 x FP4 operands are not built");
     if (!aligned16(qa) || !aligned16(qb)) return fail(MX_ERR_ALIGNMENT, "qa and qb must be 16-byte aligned");

@@ -157,7 +157,8 @@ mx_status mx_quantize_dual_layout(const void* x, int32_t src_dtype, int64_t rows
  * c:      [M][N] with row stride ldc >= N elements, MX_OUT_F32 or
  *         MX_OUT_BF16 (round to nearest even).
  * Supported pairs: fa, fb both FP8 (E4M3/E5M2 in any combination) or
- *         both E2M1.  M, N > 0; K > 0 and K % 32 == 0.
+ *         both E2M1.  0 < M, N < 2^31 - 256 (and fewer than 2^31 output
+ *         tiles of 256x256); 0 < K <= 2^23 and K % 32 == 0.
  * Errors: MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED (mixed FP8/FP4),
  *         MX_ERR_ALIGNMENT (qa, qb not 16-byte aligned), MX_ERR_HIP.
  */

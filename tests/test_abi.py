@@ -111,6 +111,10 @@ def _g(lib, qa=FAKE, sa=FAKE, ta=None, fa=0, qb=FAKE, sb=FAKE, tb=None, fb=0, M=
     (dict(qa=FAKE_ODD), mx.MX_ERR_ALIGNMENT),
     (dict(c=FAKE + 1), mx.MX_ERR_ALIGNMENT),
     (dict(ta=FAKE + 2), mx.MX_ERR_ALIGNMENT),
+    (dict(K=(1 << 23) + 32), mx.MX_ERR_INVALID_ARG),      # 32-bit tile offsets
+    (dict(M=1 << 31), mx.MX_ERR_INVALID_ARG),
+    (dict(N=(1 << 31) - 255), mx.MX_ERR_INVALID_ARG),
+    (dict(M=1 << 30, N=1 << 30), mx.MX_ERR_INVALID_ARG),  # 2^40 tiles
 ])
 def test_gemm_validation(lib, kw, status):
     assert _g(lib, **kw) == status
