@@ -104,6 +104,11 @@ class Timer:
     def mean_ms(self, name):
         return float(np.mean([s.elapsed_time(e) for s, e in self.samples[name]]))
 
+    def spread_ms(self, name):
+        """(median, min) of the calls' durations."""
+        v = [s.elapsed_time(e) for s, e in self.samples[name]]
+        return float(np.median(v)), float(np.min(v))
+
 
 # ------------------------------------------------------------------ workloads
 def setup_moss(args):
@@ -576,7 +581,9 @@ def main():
     quant = {}
     for n, b in info["qbytes"].items():
         gbs = b / (kernel_ms[n] * 1e-3) / 1e9
-        quant[n] = {"ms": round(kernel_ms[n], 4), "GB/s": round(gbs, 1),
+        med, mn = t.spread_ms(n)
+        quant[n] = {"ms": round(kernel_ms[n], 4), "ms_median": round(med, 4), "ms_min": round(mn, 4),
+                    "GB/s": round(gbs, 1),
                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(b)}
     if info["gemm_kernel"]:
         gk = info["gemm_kernel"]
@@ -617,11 +624,16 @@ def main():
     if info["gemm_kernel"]:
         out["kernels"]["gemm"] = {"ms": round(g_ms, 4), "TFLOP/s": roofline["achieved"],
                                   "frac_mfma": roofline["frac"]}
+        if not isinstance(info["gemm_kernel"], list):
+            med, mn = t.spread_ms(info["gemm_kernel"])
+            out["kernels"]["gemm"].update({"ms_median": round(med, 4), "ms_min": round(mn, 4)})
         if isinstance(info["gemm_kernel"], list):
             for g in info["gemms"]:
                 n, M, N, K = g[0], g[7], g[8], g[9]
                 tf = 2.0 * M * N * K / (kernel_ms[n] * 1e-3) / 1e12
-                out["kernels"][n] = {"ms": round(kernel_ms[n], 4), "MNK": [M, N, K], "TFLOP/s": round(tf, 1),
+                med, mn = t.spread_ms(n)
+                out["kernels"][n] = {"ms": round(kernel_ms[n], 4), "ms_median": round(med, 4), "ms_min": round(mn, 4),
+                                     "MNK": [M, N, K], "TFLOP/s": round(tf, 1),
                                      "frac_mfma": round(tf / MFMA_PEAK_TFLOPS[info["mfma"]], 4)}
             out["roofline"]["algorithmic"] = (f"{info['flops']:.4g} FLOP over the six launches of one step "
                                               "(achieved = that / the sum of their mean durations)")
