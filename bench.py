@@ -545,7 +545,7 @@ def main():
                         "lands in the first timed kernel, so the default evicts by reading")
     args = p.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
+        print("bench.py measures one MI355X: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
     assert torch.cuda.is_available(), "needs a GPU"
