@@ -47,7 +47,10 @@ template <int FMT> struct Range;
 template <> struct Range<E4M3> { static constexpr float log2r = 17.8073549f; };
 template <> struct Range<E5M2> { static constexpr float log2r = 31.8073549f; };
 
-// log2 of x > 0 (finite or +Inf)
+// log2 of x > 0 (finite or +Inf): x = m * 2^e with m in [sqrt(1/2),
+// sqrt(2)), z = m - 1 (exact), log2 x = e + z * P(z), P of degree 8 (a
+// least-squares fit of log2(1+z)/z on that range, coefficients rounded to
+// fp32), every step one fused multiply-add, in the order written
 __device__ __forceinline__ float log2_fixed(float x)
 {
 #pragma clang fp contract(off)
@@ -63,18 +66,21 @@ __device__ __forceinline__ float log2_fixed(float x)
         m = m * 0.5f;
         ex += 1;
     }
-    const float t = (m - 1.0f) / (m + 1.0f);
-    const float t2 = t * t;
-    // (2 / ln 2) * (t + t^3/3 + t^5/5 + t^7/7 + t^9/9), inner coefficients first
-    float s = 0.320598898f;
-    s = s * t2 + 0.412198583f;
-    s = s * t2 + 0.577078016f;
-    s = s * t2 + 0.961796694f;
-    s = s * t2 + 2.88539008f;
-    return (float)ex + t * s;
+    const float z = m - 1.0f;                        // exact
+    float p = 0x1.025a88p-3f;
+    p = __builtin_fmaf(p, z, -0x1.a8cd06p-3f);
+    p = __builtin_fmaf(p, z, 0x1.b9b144p-3f);
+    p = __builtin_fmaf(p, z, -0x1.e94efep-3f);
+    p = __builtin_fmaf(p, z, 0x1.26d40cp-2f);
+    p = __builtin_fmaf(p, z, -0x1.715c9cp-2f);
+    p = __builtin_fmaf(p, z, 0x1.ec73d4p-2f);
+    p = __builtin_fmaf(p, z, -0x1.71547p-1f);
+    p = __builtin_fmaf(p, z, 0x1.715476p+0f);
+    return __builtin_fmaf(z, p, (float)ex);
 }
 
-// 2^y
+// 2^y: y = n + z with n = floor(y + 1/2), z = y - n (exact), 2^z from a
+// degree-6 fit on [-1/2, 1/2] whose constant term is exactly 1, then 2^n
 __device__ __forceinline__ float exp2_fixed(float y)
 {
 #pragma clang fp contract(off)
@@ -82,16 +88,14 @@ __device__ __forceinline__ float exp2_fixed(float y)
     if (y >= 128.0f) return __builtin_inff();
     if (y < -150.0f) return 0.0f;
     const float n = floorf(y + 0.5f);
-    const float z = (y - n) * 0.693147181f;          // (fraction) * ln 2, |fraction| <= 1/2
-    // e^z = 1 + z + z^2/2 + ... + z^7/5040, Horner from the highest power
-    float s = 1.98412698e-4f;
-    s = s * z + 1.38888889e-3f;
-    s = s * z + 8.33333377e-3f;
-    s = s * z + 4.16666679e-2f;
-    s = s * z + 0.166666672f;
-    s = s * z + 0.5f;
-    s = s * z + 1.0f;
-    s = s * z + 1.0f;
+    const float z = y - n;                           // exact, |z| <= 1/2
+    float s = 0x1.41a7p-13f;
+    s = __builtin_fmaf(s, z, 0x1.5f44f4p-10f);
+    s = __builtin_fmaf(s, z, 0x1.3b2dfep-7f);
+    s = __builtin_fmaf(s, z, 0x1.c6aed6p-5f);
+    s = __builtin_fmaf(s, z, 0x1.ebfbdap-3f);
+    s = __builtin_fmaf(s, z, 0x1.62e43p-1f);
+    s = __builtin_fmaf(s, z, 1.0f);
     return ldexpf(s, (int)n);
 }
 

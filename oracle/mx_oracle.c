@@ -664,13 +664,18 @@ int or_gemm_entries(const uint8_t* qa, const uint8_t* sa, const float* ta, int f
 /*   x = sign(q) * amax * (|decode(q)| / Fmax)^(1/k).                  */
 /* The powers go through log2 and exp2.  So that the codes are a plain */
 /* function of fp32 arithmetic, both are written out as fixed fp32     */
-/* polynomial evaluations (every operation rounded once, in the order  */
-/* written): log2 from the atanh series in t = (m-1)/(m+1), exp2 from  */
-/* the Taylor series of e^(f ln 2) on [-1/2, 1/2].                     */
+/* polynomial evaluations, each step a single IEEE operation (a fused  */
+/* multiply-add where written, `fmaf`), in the order written.          */
+/* log2: x = m * 2^e with m in [sqrt(1/2), sqrt(2)), z = m - 1 (exact),*/
+/* log2(x) = e + z * P(z), P of degree 8 fitted to log2(1+z)/z on that */
+/* range (least squares on Chebyshev nodes, coefficients rounded to    */
+/* fp32; about 2 ulp).  exp2: y = n + z with n = floor(y + 1/2),       */
+/* z = y - n (exact), 2^z from a degree-6 fit on [-1/2, 1/2] with a     */
+/* constant term of exactly 1 (about 1.3 ulp), then 2^n by ldexp.      */
 /* ------------------------------------------------------------------ */
 float or_log2_fp32(float x)
 {
-    /* x > 0 finite.  x = m * 2^e with m in [sqrt(1/2), sqrt(2)) */
+    /* x > 0 (finite or +Inf) */
     int e = 0;
     if (x < 0x1p-126f) { x = x * 0x1p32f; e = -32; }          /* subnormal: exact scaling */
     uint32_t b;
@@ -680,15 +685,17 @@ float or_log2_fp32(float x)
     float m;
     memcpy(&m, &b, 4);
     if (m > 1.41421356f) { m = m * 0.5f; e += 1; }
-    const float t = (m - 1.0f) / (m + 1.0f);
-    const float t2 = t * t;
-    /* 2/ln2 * (t + t^3/3 + ... + t^9/9) */
-    float p = 0.320598898f;
-    p = p * t2 + 0.412198583f;
-    p = p * t2 + 0.577078016f;
-    p = p * t2 + 0.961796694f;
-    p = p * t2 + 2.88539008f;
-    return (float)e + t * p;
+    const float z = m - 1.0f;                                  /* exact (Sterbenz) */
+    float p = 0x1.025a88p-3f;
+    p = fmaf(p, z, -0x1.a8cd06p-3f);
+    p = fmaf(p, z, 0x1.b9b144p-3f);
+    p = fmaf(p, z, -0x1.e94efep-3f);
+    p = fmaf(p, z, 0x1.26d40cp-2f);
+    p = fmaf(p, z, -0x1.715c9cp-2f);
+    p = fmaf(p, z, 0x1.ec73d4p-2f);
+    p = fmaf(p, z, -0x1.71547p-1f);
+    p = fmaf(p, z, 0x1.715476p+0f);
+    return fmaf(z, p, (float)e);
 }
 
 float or_exp2_fp32(float y)
@@ -697,15 +704,14 @@ float or_exp2_fp32(float y)
     if (y >= 128.0f) return INFINITY;
     if (y < -150.0f) return 0.0f;
     const float n = floorf(y + 0.5f);
-    const float z = (y - n) * 0.693147181f;                    /* f ln 2, |f| <= 1/2 */
-    float p = 1.98412698e-4f;                                  /* 1/5040 */
-    p = p * z + 1.38888889e-3f;                                /* 1/720 */
-    p = p * z + 8.33333377e-3f;                                /* 1/120 */
-    p = p * z + 4.16666679e-2f;                                /* 1/24 */
-    p = p * z + 0.166666672f;                                  /* 1/6 */
-    p = p * z + 0.5f;
-    p = p * z + 1.0f;
-    p = p * z + 1.0f;
+    const float z = y - n;                                     /* exact, |z| <= 1/2 */
+    float p = 0x1.41a7p-13f;
+    p = fmaf(p, z, 0x1.5f44f4p-10f);
+    p = fmaf(p, z, 0x1.3b2dfep-7f);
+    p = fmaf(p, z, 0x1.c6aed6p-5f);
+    p = fmaf(p, z, 0x1.ebfbdap-3f);
+    p = fmaf(p, z, 0x1.62e43p-1f);
+    p = fmaf(p, z, 1.0f);
     return ldexpf(p, (int)n);
 }
 
