@@ -34,6 +34,8 @@
 // the code alone.  One thread handles 4 consecutive elements (16-byte loads,
 // 4-byte code stores); the G/4 threads of a group reduce amax and amin with
 // lane shuffles inside their wave.
+#include <type_traits>
+
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -136,20 +138,37 @@ __global__ __launch_bounds__(256) void k_optstate_quant(const float4* __restrict
         const bool live = t < nthreads;
         const float4 v = live ? x[t] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         const float a[4] = {fabsf(v.x), fabsf(v.y), fabsf(v.z), fabsf(v.w)};
-        float amax = 0.0f, amin = __builtin_inff();
-        uint32_t bad = 0;
+        // group maximum as an integer maximum of |x|'s bits (the order of the
+        // values for finite magnitudes; Inf and NaN bits lie above every
+        // finite one, so they flag the group by themselves), and the
+        // smallest nonzero magnitude
+        uint32_t kmax = 0;
+        float amin = __builtin_inff();
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            bad |= (a[i] == a[i] && a[i] != __builtin_inff()) ? 0u : 1u;
-            amax = fmaxf(amax, a[i]);
+            kmax = max(kmax, __float_as_uint(a[i]));
             if (a[i] > 0.0f) amin = fminf(amin, a[i]);
         }
-#pragma unroll
-        for (int off = 1; off < T; off <<= 1) {
-            amax = fmaxf(amax, __shfl_xor(amax, off));
-            amin = fminf(amin, __shfl_xor(amin, off));
-            bad |= (uint32_t)__shfl_xor((int)bad, off);
-        }
+        // butterflies inside 32-lane halves by swizzle (xor mask in bits 14:10,
+        // and mask 0x1F), across halves by a permute
+        auto step = [&](auto OFFC) __attribute__((always_inline)) {
+            constexpr int off = decltype(OFFC)::value;
+            if constexpr (off < T && off < 32) {
+                kmax = max(kmax, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kmax, 0x1F | (off << 10)));
+                amin = fminf(amin, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(amin), 0x1F | (off << 10))));
+            } else if constexpr (off < T) {
+                kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+                amin = fminf(amin, __shfl_xor(amin, off));
+            }
+        };
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 4>{});
+        step(std::integral_constant<int, 8>{});
+        step(std::integral_constant<int, 16>{});
+        step(std::integral_constant<int, 32>{});
+        const bool bad = kmax >= 0x7F800000u;
+        const float amax = __uint_as_float(kmax);
         if (!live) continue;
         const int64_t g = t / T;
         const bool lead = (t % T) == 0;
