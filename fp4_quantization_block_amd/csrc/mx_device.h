@@ -109,26 +109,28 @@ __device__ __forceinline__ uint32_t cvt8_fp4(const float* y)
 // 2^32), round up iff u < F.  Returns the chosen value (exactly
 // representable, sign of y kept); |y| >= fmax saturates.
 // ---------------------------------------------------------------------
+//
+// Computed in fixed point from the bits of |y|: with m the biased exponent
+// of the quantum's binade (that of |y|, at least the format's emin), |y| /
+// quantum = 24-bit significand x 2^-(23 - mbits + (m - e)); placing the
+// significand at bit 32 of a 64-bit word and shifting it right by that
+// amount (at most 63: smaller values have no bits at or above 2^-32) leaves
+// floor(|y| / quantum) in the high word and F in the low one.  The lower
+// neighbour is then that integer times the quantum, the upper one the next
+// multiple, and a value at or above fmax gives at least fmax on both sides.
+// This yields the definition's F and neighbours for every finite fp32 value
+// in all three formats.
 template <int FMT>
 __device__ __forceinline__ float sr_value(float y, uint32_t u)
 {
-    const float a = fabsf(y);
-    float r;
-    if (a >= Fmt<FMT>::fmax) {
-        r = Fmt<FMT>::fmax;
-    } else {
-        const uint32_t ab = __float_as_uint(a);
-        const int ea = (int)(ab >> 23) - 127;                  // -127 for 0 / subnormal
-        const int eq = (ea > Fmt<FMT>::emin ? ea : Fmt<FMT>::emin) - Fmt<FMT>::mbits;  // quantum 2^eq
-        // lo: |y| truncated to a multiple of 2^eq
-        float lo;
-        const int drop = 23 - (ea - eq);                      // mantissa bits below the quantum
-        if (ea < eq || ab < 0x00800000u) lo = 0.0f;           // below one quantum (or fp32 subnormal)
-        else lo = __uint_as_float(ab & ~((1u << drop) - 1u));
-        const float d = (a - lo) * exp2i(32 - eq);            // exact, < 2^32
-        const uint32_t F = (uint32_t)d;                       // floor
-        r = (u < F) ? lo + exp2i(eq) : lo;
-    }
+    constexpr int MB = Fmt<FMT>::mbits, EMINB = Fmt<FMT>::emin + 127;
+    const uint32_t ab = __float_as_uint(y) & 0x7FFFFFFFu;
+    const int eb = (int)(ab >> 23);                         // 0 for zero and fp32 subnormals
+    const int m = eb > EMINB ? eb : EMINB;
+    const int rs = min(23 - MB + (m - eb), 63);
+    const uint64_t X = ((uint64_t)((ab & 0x007FFFFFu) | 0x00800000u) << 32) >> rs;
+    const uint32_t n = (uint32_t)(X >> 32) + ((u < (uint32_t)X) ? 1u : 0u);
+    const float r = fminf(ldexpf((float)n, m - 127 - MB), Fmt<FMT>::fmax);
     return __builtin_copysignf(r, y);
 }
 
