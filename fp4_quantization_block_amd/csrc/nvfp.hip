@@ -36,6 +36,8 @@
 // matrix peak is a quarter of the FP4 one.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -571,14 +573,22 @@ __global__ __launch_bounds__(256) void k_nv_dequant(const uint8_t* q, const uint
 // k_nv_gemm: C = alpha * sA(i) * sB(j) * sum_k Ahat[i][k] Bhat[j][k] on nvfp
 // operands (A [M][K] and B [N][K] row copies as the quantizer writes them;
 // sA(i), sB(j) the second-level scale of the row's domain).  256x256 tile
-// per 256-thread workgroup, one wave per SIMD computing a 128x128 quarter
-// (4x4 f16 MFMA 32x32x16 tiles, all 256 accumulators); K advances 64
-// elements per stage.  Each stage's codes and block scales are loaded into
-// registers a stage ahead, dequantized exactly to f16 (converter with 2^E,
-// packed multiply by the integer factor), and written to the other of two
-// LDS stage buffers (rows of 128 bytes whose 16-byte chunks are
-// XOR-swizzled by (row >> 1) & 7, conflict-free for the fragment reads).
-// The second-level scales are applied once per output in the epilogue.
+// per 512-thread workgroup, K advancing 64 elements per stage.  Each stage's
+// codes and block scales are dequantized exactly to f16 (converter with 2^E,
+// packed multiply by the integer factor) into one of two LDS stage buffers
+// (rows of 128 bytes whose 16-byte chunks are XOR-swizzled by
+// (row >> 1) & 7, conflict-free for the fragment reads), and multiplied on
+// the f16 matrix cores (32x32x16) with fp32 accumulation.
+//
+// Two waves per SIMD in two groups (waves 0-3 and 4-7; wave w runs on SIMD
+// w % 4): each wave computes a 128x64 piece of its SIMD's 128x128 quarter.
+// A stage takes two phases separated by workgroup barriers; in each, one
+// group multiplies the stage from LDS while the other dequantizes its half
+// of the next stage (A and B rows 128 g .. 128 g + 127 for group g) into
+// the other buffer and loads its half of a later stage into registers.  The SIMD thus overlaps one wave's MFMAs with the other's
+// conversions, LDS writes and loads (a probe: VALU work of one wave runs
+// under another wave's MFMAs at no cost in cycles).  The second-level
+// scales and alpha are applied once per output in the epilogue.
 // ---------------------------------------------------------------------------
 // workgroup barrier that waits for this wave's LDS traffic only (not for
 // its global loads, which a fence-carrying __syncthreads would drain)
@@ -615,22 +625,30 @@ __device__ __forceinline__ void nv_dequant_chunk(uint8_t* tile, int row, int hal
 }
 
 template <int OUTT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_nv_gemm(NvGemmJob g, int tiles_m, int tiles_n)
 {
-    __shared__ __align__(16) uint8_t lA[2][NBM * NROWB];
-    __shared__ __align__(16) uint8_t lB[2][NBM * NROWB];
+    // stage buffer b: the A tile at b * 64 KiB, the B tile 32 KiB after it
+    // (within reach of an LDS instruction's immediate offset)
+    __shared__ __align__(16) uint8_t lds[2 * 2 * NBM * NROWB];
+    auto tA = [&](int b) __attribute__((always_inline)) { return lds + b * (2 * NBM * NROWB); };
+    auto tB = [&](int b) __attribute__((always_inline)) { return lds + b * (2 * NBM * NROWB) + NBM * NROWB; };
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
+    const int grp = wave >> 2, q = wave & 3;
+    const int wm = q >> 1, wn = q & 1, h = lane >> 5, l32 = lane & 31;
+    const int gt = tid & 255;                        // thread index inside the group
 
     // tile order: workgroups dealt round-robin to the 8 XCDs; each XCD takes a
     // contiguous range of tiles in row-major order of 4-row groups
     int t = blockIdx.x;
     const int total = tiles_m * tiles_n;
     if (total % 8 == 0) t = (t % 8) * (total / 8) + t / 8;
-    const int grp = 4 * tiles_n, first = (t / grp) * 4, nrows = min(4, tiles_m - first);
-    const int tm = first + (t % grp) % nrows, tn = (t % grp) / nrows;
+    const int grw = 4 * tiles_n, first = (t / grw) * 4, nrows = min(4, tiles_m - first);
+    // (the tile indices are wave-uniform; saying so keeps the buffer
+    // descriptors in scalar registers)
+    const int tm = __builtin_amdgcn_readfirstlane(first + (t % grw) % nrows);
+    const int tn = __builtin_amdgcn_readfirstlane((t % grw) / nrows);
     const int64_t m0 = (int64_t)tm * NBM, n0 = (int64_t)tn * NBM;
     const int64_t kcb = g.K / 2, ksb = g.K / 16;
     const int nst = (int)(g.K / NBK);
@@ -644,93 +662,114 @@ void k_nv_gemm(NvGemmJob g, int tiles_m, int tiles_n)
     const auto rA = rsrc(g.qa, m0, g.M, kcb), rB = rsrc(g.qb, n0, g.N, kcb);
     const auto rSA = rsrc(g.sa, m0, g.M, ksb), rSB = rsrc(g.sb, n0, g.N, ksb);
 
-    // loads of a stage: chunk c = tid + 256 p (p = 0, 1) is row c / 2, half c % 2
+    // the thread's share of a stage: chunk c = 256 grp + gt of A and of B,
+    // i.e. tile row c / 2, 16-byte half c % 2 of the stage's 32 code bytes
+    // (two lanes read a row's 32 bytes: 16-byte pieces of separate rows
+    // load at a quarter of the rate)
+    const int crow = (256 * grp + gt) >> 1, chalf = gt & 1;
+    const uint32_t co = (uint32_t)(crow * kcb) + (uint32_t)(chalf * 16);
+    const uint32_t so = (uint32_t)(crow * ksb) + (uint32_t)(chalf * 2);
+    // two register sets of loaded codes and scales, by stage parity: a
+    // group's half of stage s+3 is loaded while it converts stage s+1, so
+    // each load has two stages to arrive
     uint4 cA[2], cB[2];
     uint32_t sA[2], sB[2];
-    auto gload = [&](int s) __attribute__((always_inline)) {
-#pragma unroll
-        for (int p = 0; p < 2; p++) {
-            const int c = tid + 256 * p, row = c >> 1, half = c & 1;
-            const uint32_t co = (uint32_t)(row * kcb) + (uint32_t)(half * 16);
-            const uint32_t so = (uint32_t)(row * ksb) + (uint32_t)(half * 2);
-            cA[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rA, co, s * 32, 0));
-            cB[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rB, co, s * 32, 0));
-            sA[p] = __builtin_amdgcn_raw_buffer_load_b16(rSA, so, s * 4, 0);
-            sB[p] = __builtin_amdgcn_raw_buffer_load_b16(rSB, so, s * 4, 0);
-        }
+    auto gload = [&](auto PC, int s) __attribute__((always_inline)) {
+        constexpr int P = decltype(PC)::value;
+        cA[P] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rA, co, s * 32, 0));
+        cB[P] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rB, co, s * 32, 0));
+        sA[P] = __builtin_amdgcn_raw_buffer_load_b16(rSA, so, s * 4, 0);
+        sB[P] = __builtin_amdgcn_raw_buffer_load_b16(rSB, so, s * 4, 0);
     };
-    auto dq_write = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int p = 0; p < 2; p++) {
-            const int c = tid + 256 * p, row = c >> 1, half = c & 1;
-            nv_dequant_chunk(lA[buf], row, half, cA[p], sA[p]);
-            nv_dequant_chunk(lB[buf], row, half, cB[p], sB[p]);
-        }
+    auto dq_write = [&](auto PC, int buf) __attribute__((always_inline)) {
+        constexpr int P = decltype(PC)::value;
+        // the row goes through an empty asm so that its LDS addresses are
+        // formed here, in the conversion phase, rather than held in registers
+        // across the loop
+        int r = crow;
+        asm volatile("" : "+v"(r));
+        nv_dequant_chunk(tA(buf), r, chalf, cA[P], sA[P]);
+        nv_dequant_chunk(tB(buf), r, chalf, cB[P], sB[P]);
     };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
 
-    f16acc acc[4][4];
+    f16acc acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-    gload(0);
-    dq_write(0);
-    if (nst > 1) gload(1);
+    // stage 0 by both groups, then each group's halves of stages 1 and 2 in flight
+    gload(P0{}, 0);
+    dq_write(P0{}, 0);
+    if (nst > 1) gload(P1{}, 1);
+    if (nst > 2) gload(P0{}, 2);
     lds_barrier();
-    // fragments of k-step ks of buffer `buf`: A tiles 0..3, B tiles 0..3 of the wave
-    struct Frag { h8 a[4], b[4]; };
+    // fragments of k-step ks of buffer `buf`: A tiles 0..3 and B tiles 0..1 of the wave
+    struct Frag { h8 a[4], b[2]; };
+    const int arow = wm * 128 + l32, brow = wn * 128 + grp * 64 + l32;
     auto rd_frags = [&](Frag& f, int buf, int ks) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            f.a[i] = *(const h8*)(lA[buf] + nv_swz(wm * 128 + i * 32 + l32, 2 * ks + h));
-            f.b[i] = *(const h8*)(lB[buf] + nv_swz(wn * 128 + i * 32 + l32, 2 * ks + h));
-        }
+        for (int i = 0; i < 4; i++) f.a[i] = *(const h8*)(tA(buf) + nv_swz(arow + i * 32, 2 * ks + h));
+#pragma unroll
+        for (int j = 0; j < 2; j++) f.b[j] = *(const h8*)(tB(buf) + nv_swz(brow + j * 32, 2 * ks + h));
     };
     auto mmas = [&](const Frag& f) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < 2; j++)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     };
-    // each k-step's fragments are read while the previous k-step's 16 MFMAs
+    // each k-step's fragments are read while the previous k-step's MFMAs
     // run (two register sets); the fences keep the reads ahead of the MFMAs
     Frag F0, F1;
-    for (int s = 0; s < nst; s++) {
-        const int cur = s & 1;
-        rd_frags(F0, cur, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        rd_frags(F1, cur, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mmas(F0);
-        __builtin_amdgcn_sched_barrier(0);
-        rd_frags(F0, cur, 2);
-        __builtin_amdgcn_sched_barrier(0);
-        mmas(F1);
-        __builtin_amdgcn_sched_barrier(0);
-        rd_frags(F1, cur, 3);
-        __builtin_amdgcn_sched_barrier(0);
-        mmas(F0);
-        __builtin_amdgcn_sched_barrier(0);
-        mmas(F1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < nst) {
-            dq_write(cur ^ 1);                       // stage s+1 into the buffer stage s-1 used
-            if (s + 2 < nst) gload(s + 2);
+    // stage s (parity P = s & 1): buffer P holds it; the converting group
+    // writes its half of stage s+1 into buffer P^1 from register set P^1,
+    // then loads its half of stage s+3 into that set
+    auto stage = [&](auto PC, int s) __attribute__((always_inline)) {
+        constexpr int P = decltype(PC)::value;
+        using Q = std::integral_constant<int, P ^ 1>;
+        for (int p = 0; p < 2; p++) {
+            if (grp == p) {
+                rd_frags(F0, P, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                rd_frags(F1, P, 1);
+                __builtin_amdgcn_sched_barrier(0);
+                mmas(F0);
+                __builtin_amdgcn_sched_barrier(0);
+                rd_frags(F0, P, 2);
+                __builtin_amdgcn_sched_barrier(0);
+                mmas(F1);
+                __builtin_amdgcn_sched_barrier(0);
+                rd_frags(F1, P, 3);
+                __builtin_amdgcn_sched_barrier(0);
+                mmas(F0);
+                __builtin_amdgcn_sched_barrier(0);
+                mmas(F1);
+                __builtin_amdgcn_sched_barrier(0);
+            } else if (s + 1 < nst) {
+                dq_write(Q{}, P ^ 1);                // this group's half of stage s+1
+                if (s + 3 < nst) gload(Q{}, s + 3);
+            }
+            // LDS hand-off only: the loads stay in flight across it
+            lds_barrier();
         }
-        // LDS hand-off only: the loads of stage s+2 stay in flight across it
-        lds_barrier();
+    };
+    for (int s = 0; s < nst; s += 2) {
+        stage(P0{}, s);
+        if (s + 1 < nst) stage(P1{}, s + 1);
     }
 
     // epilogue: alpha and the two second-level scales once per output
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int64_t col = n0 + wn * 128 + j * 32 + l32;
+        for (int j = 0; j < 2; j++) {
+            const int64_t col = n0 + wn * 128 + grp * 64 + j * 32 + l32;
             if (col >= g.N) continue;
             const float sbv = g.tb[g.lb ? col / NV_PANEL : 0];
 #pragma unroll
@@ -825,8 +864,8 @@ hipError_t launch_nv_gemm(const NvGemmJob& j, hipStream_t stream)
 {
     const int tiles_m = (int)((j.M + NBM - 1) / NBM), tiles_n = (int)((j.N + NBM - 1) / NBM);
     const unsigned grid = (unsigned)(tiles_m * tiles_n);
-    if (j.out_dtype == 0) k_nv_gemm<0><<<grid, 256, 0, stream>>>(j, tiles_m, tiles_n);
-    else k_nv_gemm<1><<<grid, 256, 0, stream>>>(j, tiles_m, tiles_n);
+    if (j.out_dtype == 0) k_nv_gemm<0><<<grid, 512, 0, stream>>>(j, tiles_m, tiles_n);
+    else k_nv_gemm<1><<<grid, 512, 0, stream>>>(j, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
