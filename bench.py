@@ -66,10 +66,10 @@ MEASURED_TRAFFIC = {
     "dual": {"source": "quant.hip", "sha256": "b18754e66b4322bd",
              "fetch_kib": 229549.2, "write_kib": 496622.1},
     # k_nv_gemm
-    "nvfp_global": {"source": "nvfp.hip", "sha256": "12fa371ea1a3a812",
-                    "fetch_kib": 195547.2, "write_kib": 229500.6},
-    "nvfp_local": {"source": "nvfp.hip", "sha256": "12fa371ea1a3a812",
-                   "fetch_kib": 195549.9, "write_kib": 229530.2},
+    "nvfp_global": {"source": "nvfp.hip", "sha256": "db29b3bad8a50855",
+                    "fetch_kib": 193854.3, "write_kib": 232288.5},
+    "nvfp_local": {"source": "nvfp.hip", "sha256": "db29b3bad8a50855",
+                   "fetch_kib": 193857.4, "write_kib": 232298.3},
     # k_optstate_quant (the slower of the step's two kernels)
     "coat": {"source": "optstate.hip", "sha256": "48a84d40d196f9f8",
              "fetch_kib": 229452.1, "write_kib": 122898.1},

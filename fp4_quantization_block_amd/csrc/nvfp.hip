@@ -662,11 +662,15 @@ void k_nv_gemm(NvGemmJob g, int tiles_m, int tiles_n)
     const auto rA = rsrc(g.qa, m0, g.M, kcb), rB = rsrc(g.qb, n0, g.N, kcb);
     const auto rSA = rsrc(g.sa, m0, g.M, ksb), rSB = rsrc(g.sb, n0, g.N, ksb);
 
-    // the thread's share of a stage: chunk c = 256 grp + gt of A and of B,
-    // i.e. tile row c / 2, 16-byte half c % 2 of the stage's 32 code bytes
-    // (two lanes read a row's 32 bytes: 16-byte pieces of separate rows
-    // load at a quarter of the rate)
-    const int crow = (256 * grp + gt) >> 1, chalf = gt & 1;
+    // the thread's share of a stage: 16-byte half gt % 2 of the stage's 32
+    // code bytes of one tile row of A and of B, rows 128 grp .. 128 grp + 127.
+    // Two lanes read a row's 32 bytes (16-byte pieces of separate rows load
+    // at a quarter of the rate).  Each 16 lanes cover 8 rows, the even ones in
+    // lanes 0-7 and the odd ones in lanes 8-15: rows 2j and 2j+1 share a
+    // swizzle key, and 8 lanes that write one chunk of four rows of distinct
+    // keys hit distinct banks (a probe: 13 cycles per 1 KiB written, as for
+    // contiguous writes, against 16 with consecutive rows in lanes 0-7).
+    const int crow = 128 * grp + (gt >> 4) * 8 + ((gt >> 1) & 3) * 2 + ((gt >> 3) & 1), chalf = gt & 1;
     const uint32_t co = (uint32_t)(crow * kcb) + (uint32_t)(chalf * 16);
     const uint32_t so = (uint32_t)(crow * ksb) + (uint32_t)(chalf * 2);
     // two register sets of loaded codes and scales, by stage parity: a
