@@ -186,6 +186,14 @@ def test_gemm_one_stage_and_tiny():
     _gemm_case(rng, 33, 257, 64, False, True, mx.MX_OUT_F32, -2.0, "nvfp gemm 33x257x64")
 
 
+@pytest.mark.parametrize("K", [128, 192, 320])
+def test_gemm_few_and_odd_stages(K):
+    """2, 3 and 5 K stages of 64: the stage loop runs in pairs and loads two
+    stages ahead, so short and odd stage counts take its edge paths."""
+    rng = np.random.default_rng(41 + K)
+    _gemm_case(rng, 130, 300, K, True, False, mx.MX_OUT_BF16, 0.5, f"nvfp gemm 130x300x{K}")
+
+
 def test_gemm_nan_scale_propagates():
     """A NaN second-level scale (its domain held a NaN) makes exactly the
     outputs that use that domain NaN."""
