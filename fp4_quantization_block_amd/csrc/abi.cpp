@@ -295,6 +295,8 @@ mx_status mx_gemm_nvfp(const uint8_t* qa, const uint8_t* sa, const float* ta, in
     if (K % 64 != 0) return fail(MX_ERR_INVALID_ARG, "K must be a multiple of 64");
     if (K > (int64_t)1 << 24) return fail(MX_ERR_INVALID_ARG, "K must be <= 2^24");
     if (M > ((int64_t)1 << 31) - 256 || N > ((int64_t)1 << 31) - 256) return fail(MX_ERR_INVALID_ARG, "M and N must be < 2^31 - 256");
+    if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t)1 << 31)
+        return fail(MX_ERR_INVALID_ARG, "M x N must be fewer than 2^31 output tiles of 256 x 256");
     if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return fail(MX_ERR_INVALID_ARG, "unknown output dtype");
     if (ldc < N) return fail(MX_ERR_INVALID_ARG, "ldc must be >= N");
     if (!aligned16(qa) || !aligned16(qb)) return fail(MX_ERR_ALIGNMENT, "qa and qb must be 16-byte aligned");

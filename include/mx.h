@@ -364,7 +364,8 @@ mx_status mx_dequantize_nvfp(const uint8_t* q, const uint8_t* scales, const floa
  * 32, so the kernel dequantizes each stage exactly to f16 and multiplies
  * on the f16 matrix cores with fp32 accumulation; alpha * sA(i) * sB(j) is
  * one fp32 factor per output, applied once.
- * K: a multiple of 64, at most 2^24.  M, N: any size.  qa, qb 16-byte
+ * K: a multiple of 64, at most 2^24.  0 < M, N < 2^31 - 256, and fewer
+ * than 2^31 output tiles of 256 x 256.  qa, qb 16-byte
  * aligned; sa, sb, ta, tb 4-byte aligned.  c: fp32 or bf16 (round to
  * nearest even), leading dimension ldc >= N.
  * Errors: MX_ERR_INVALID_ARG, MX_ERR_ALIGNMENT, MX_ERR_HIP.

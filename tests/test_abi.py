@@ -120,6 +120,25 @@ def test_gemm_validation(lib, kw, status):
     assert _g(lib, **kw) == status
 
 
+def _gnv(lib, M=64, N=64, K=64, la=0, lb=0, out=1, ldc=None, c=FAKE):
+    return lib.mx_gemm_nvfp(FAKE, FAKE, FAKE, la, FAKE, FAKE, FAKE, lb, M, N, K, 1.0, c, out,
+                            N if ldc is None else ldc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(c=None), mx.MX_ERR_INVALID_ARG),
+    (dict(la=2), mx.MX_ERR_INVALID_ARG),
+    (dict(out=3), mx.MX_ERR_INVALID_ARG),
+    (dict(K=96), mx.MX_ERR_INVALID_ARG),                   # K % 64
+    (dict(K=(1 << 24) + 64), mx.MX_ERR_INVALID_ARG),
+    (dict(M=1 << 31), mx.MX_ERR_INVALID_ARG),
+    (dict(M=1 << 30, N=1 << 30), mx.MX_ERR_INVALID_ARG),   # 2^44 output tiles
+    (dict(ldc=32), mx.MX_ERR_INVALID_ARG),
+])
+def test_gemm_nvfp_validation(lib, kw, status):
+    assert _gnv(lib, **kw) == status
+
+
 def test_dequantize_validation(lib):
     f = lib.mx_dequantize
     assert f(None, FAKE, None, 0, 64, 64, 0, 0, FAKE, 0, None) == mx.MX_ERR_INVALID_ARG
