@@ -666,7 +666,7 @@ int or_gemm_entries(const uint8_t* qa, const uint8_t* sa, const float* ta, int f
 /* function of fp32 arithmetic, both are written out as fixed fp32     */
 /* polynomial evaluations, each step a single IEEE operation (a fused  */
 /* multiply-add where written, `fmaf`), in the order written.          */
-/* log2: x = m * 2^e with m in [sqrt(1/2), sqrt(2)), z = m - 1 (exact),*/
+/* log2: x = m * 2^e with m in (sqrt(1/2), sqrt(2)), z = m - 1 (exact),*/
 /* log2(x) = e + z * P(z), P of degree 8 fitted to log2(1+z)/z on that */
 /* range (least squares on Chebyshev nodes, coefficients rounded to    */
 /* fp32; about 2 ulp).  exp2: y = n + z with n = floor(y + 1/2),       */
