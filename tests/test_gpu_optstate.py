@@ -77,6 +77,24 @@ def test_degenerate_groups(fmt):
     _compare(x, fmt, 128, f"{fmt} degenerate")
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_dequantize_any_parameters(fmt):
+    """Every code under per-group parameters no quantizer produces: k of 0,
+    negative, tiny, huge or infinite, and amax negative, zero, subnormal or
+    infinite.  The powers then overflow, underflow or turn NaN, and the
+    dequantizer must take each case as the oracle does."""
+    params = [(1.0, 0.0), (1.0, -2.0), (1.0, np.inf), (1.0, 1e-30), (1.0, 1e30), (-3.0, 0.5), (np.inf, 1.0),
+              (0.0, 1.0), (2.0 ** -140, 3.0), (1e30, 0.05), (7.5, 1.0), (1.0, -np.inf)]
+    group = 256
+    q = np.tile(np.arange(256, dtype=np.uint8), len(params))
+    amax = np.array([a for a, _ in params], np.float32)
+    k = np.array([kk for _, kk in params], np.float32)
+    back = mx.mx_dequantize_optstate(torch.from_numpy(q).to(DEV), torch.from_numpy(amax).to(DEV),
+                                     torch.from_numpy(k).to(DEV), fmt, group)
+    torch.cuda.synchronize()
+    assert_same_f32(back.cpu().numpy(), O.optstate_dequantize(q, amax, k, fmt, group))
+
+
 @pytest.mark.parametrize("n_groups", [1, 3, 63, 1025])
 def test_ragged_grid(n_groups):
     """Group counts that leave waves and workgroups partly empty."""
