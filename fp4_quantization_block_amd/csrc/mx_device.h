@@ -188,6 +188,39 @@ __device__ __forceinline__ void fwht32(float* v)
     }
 }
 
+// fwht32 that also returns the |max| key of its output.  Of the last
+// stage's pair, max(|RN(a+b)|, |RN(a-b)|) = RN(|a|+|b|): one of the two is
+// the sum of the magnitudes and the other their difference, and rounding to
+// nearest is monotone and odd-symmetric.  So 16 sums of magnitudes give the
+// key instead of 32 abs-max steps.  A block holding a NaN or an Inf, or
+// whose transform overflows, gets a key of at least 0x7F800000 either way
+// (Inf - Inf gives an Inf key here where the output holds a NaN).
+__device__ __forceinline__ uint32_t fwht32_key(float* v)
+{
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+        const int h = 1 << st;
+#pragma unroll
+        for (int i = 0; i < 32; i++)
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    }
+    uint32_t key = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const float a = v[i], b = v[i + 16];
+        v[i] = a + b;
+        v[i + 16] = a - b;
+        // the sums are +0 or more, or NaN: the largest raw pattern,
+        // its sign cleared, is the key
+        key = max(key, __float_as_uint(fabsf(a) + fabsf(b)));
+    }
+    return key & 0x7FFFFFFFu;
+}
+
 // ---------------------------------------------------------------------------
 // x / s_t rounded to nearest even, with the divisor s_t shared by many
 // quotients (a tensor scale, a group maximum).  The

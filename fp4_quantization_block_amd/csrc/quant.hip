@@ -109,8 +109,8 @@ __device__ __forceinline__ uint32_t block_values(Elem&& elem, bool two_level, bo
         have = true;
     }
     if (had) {
-        fwht32(v);
-        have = false;
+        key = fwht32_key(v);
+        have = true;
     }
     if (!have) {
         key = 0;

@@ -116,6 +116,7 @@ def test_nonfinite_and_degenerate_blocks(src):
     x[36, :32] = 3.4e38                   # near fp32 max
     x[37, :32] = 240.0                    # 1.875 * 2^7: saturates in E4M3
     x[38, :32] = -250.0                   # rounds past 448 * 2^-1 after scaling: saturates
+    x[39, :2] = np.inf                    # Inf - Inf inside the Hadamard transform
     if src == "bf16":                     # bf16 source: the packed-pair encoder for FP8 copies
         x = I.to_bf16_bits(x)
     for fmt in FMTS:
