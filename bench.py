@@ -60,11 +60,11 @@ MEASURED_TRAFFIC = {
     "c1": {"source": "gemm.hip", "sha256": "67670a25d4abdb9c",
            "fetch_kib": 81.7, "write_kib": 128.0},
     # the prediction call (k_amax_partial2 + k_predict_scale)
-    "autoscale": {"source": "quant.hip", "sha256": "b18754e66b4322bd",
-                  "fetch_kib": 32815.3, "write_kib": 32.1},
+    "autoscale": {"source": "quant.hip", "sha256": "64f4e1144aaa3582",
+                  "fetch_kib": 32815.3, "write_kib": 32.0},
     # the dual-layout quantizer (k_quant_tile_dma)
-    "dual": {"source": "quant.hip", "sha256": "b18754e66b4322bd",
-             "fetch_kib": 229549.2, "write_kib": 496622.1},
+    "dual": {"source": "quant.hip", "sha256": "64f4e1144aaa3582",
+             "fetch_kib": 229533.1, "write_kib": 496635.9},
     # k_nv_gemm
     "nvfp_global": {"source": "nvfp.hip", "sha256": "db29b3bad8a50855",
                     "fetch_kib": 193854.3, "write_kib": 232288.5},
