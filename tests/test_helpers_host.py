@@ -1,5 +1,7 @@
-"""CPU checks of the GPU tests' own helpers: the vectorised bf16 rounding
-against the oracle's scalar routine, and the stratified output sampler."""
+"""CPU checks of host-side facts the GPU code and tests lean on: the
+vectorised bf16 rounding against the oracle's scalar routine, the stratified
+output sampler, and the fp32 identity behind the Hadamard quantizers' block
+maximum."""
 import numpy as np
 
 import oracle as O
@@ -32,3 +34,34 @@ def test_tile_samples_cover_every_tile_with_corners():
             r1, c1 = min(r0 + 128, M) - 1, min(c0 + 128, N) - 1
             got = set(zip(ii.tolist(), jj.tolist()))
             assert {(r0, c0), (r0, c1), (r1, c0), (r1, c1)} <= got
+
+
+def _key(x):
+    return x.view(np.uint32) & np.uint32(0x7FFFFFFF)
+
+
+def test_butterfly_pair_max_is_sum_of_magnitudes():
+    # The Hadamard quantizers take a block's |max| from the transform's last
+    # stage: of a pair (a + b, a - b) rounded to fp32, the larger magnitude is
+    # RN(|a| + |b|).  Checked here in IEEE float32 over wide exponents, exact
+    # ties, subnormals, overflow and the non-finite cases, where only "at
+    # least Inf" is needed.
+    rng = np.random.default_rng(7)
+    n = 400000
+    with np.errstate(over="ignore"):          # a few draws overflow to +-Inf in the cast
+        a = (rng.standard_normal(n) * np.exp2(rng.integers(-150, 128, n))).astype(np.float32)
+        b = (rng.standard_normal(n) * np.exp2(rng.integers(-150, 128, n))).astype(np.float32)
+    # near neighbours (cancellation), equal magnitudes, and ulp-level ties
+    with np.errstate(over="ignore"):
+        c = a[: n // 4] * np.float32(1 + 2.0 ** -20)
+    d = np.nextafter(a[: n // 4], np.float32(np.inf))
+    a = np.concatenate([a, a[: n // 4], a[: n // 4], a[: n // 4], np.float32([3e38, -3e38, np.inf, np.inf, np.nan, 1e-45, 0.0, -0.0])])
+    b = np.concatenate([b, c, -d, a[: n // 4] * np.float32(2.0 ** -24), np.float32([3e38, 3e38, -np.inf, 1.0, 1.0, 1e-45, -0.0, -0.0])])
+    with np.errstate(over="ignore", invalid="ignore"):
+        s, t = a + b, a - b
+        m = np.abs(a) + np.abs(b)
+    both = np.maximum(_key(s), _key(t))
+    finite = np.isfinite(s) & np.isfinite(t)
+    assert np.array_equal(both[finite], _key(m)[finite])
+    assert (_key(m)[~finite] >= 0x7F800000).all() and (both[~finite] >= 0x7F800000).all()
+    assert (~finite).sum() >= 4
